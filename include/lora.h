@@ -1,0 +1,236 @@
+/*
+ * lora.h -- C ABI of liblora.so, the MI355X (gfx950) multi-LoRA adapter
+ * execution unit.
+ *
+ * For a batch of T tokens, each tagged with an adapter slot or with
+ * LORA_BASE_ONLY, one lora_apply call computes, per token t,
+ *
+ *     y[t] = x[t] W^T                                   (base_only)
+ *     y[t] = x[t] W^T + (alpha_i / r_i) (x[t] A_i^T) B_i^T   (slot i)
+ *
+ * over an HBM-resident pool of adapters zero-padded to a common rank.
+ *
+ * Sources (page title and section):
+ *  [P1] xpshop.cn article 492 (multi-tenant LoRA on one private base), sections
+ *       二 and 三: one resident base shared by tenants, per-tenant memory quota
+ *       as a hard boundary (over-quota mounts are refused, nothing is
+ *       evicted), the tenant is mapped to an adapter handle once at request
+ *       entry, hot-plug after weight validation, draining unload, refusal on a
+ *       base-version mismatch, routing default base_only.
+ *  [P3] "Multi-LoRA 在线服务隔离", sections on the request identity (default
+ *       deny: a missing mapping is an explicit error, never a fallback; mixed
+ *       adapters may share one batch with per-request index mapping) and on
+ *       memory accounting (reserve memory before loading; never unload
+ *       weights a request still holds).
+ *  [P4] "LLM 多 LoRA 推理服务工程 2026": four-layer runtime, the adapter
+ *       execution unit paragraph (base linear plus LoRA A/B, fused in one
+ *       launch or separate with a residual add); routing layer, the
+ *       two-level bucketing paragraph (bucket by adapter; a bucket above a
+ *       threshold runs fused, otherwise separate) and the zero-pad paragraph
+ *       (A maps hidden to rank, B maps rank to hidden; lower ranks are
+ *       zero-padded to the common rank; report the zero-pad share); SRE list
+ *       item 11 (the fused/separate threshold is tuned per GPU model).
+ *
+ * Conventions for every call:
+ *  - Every function returns an int status: LORA_OK (0) or a negative LORA_E*
+ *    code; lora_strerror() gives its text.  No call aborts the process.
+ *  - Matrices are row-major and contiguous, in the nn.Linear [out][in]
+ *    convention: W_base is [d_out][d_in], A is [rank][d_in], B is
+ *    [d_out][rank].  x is [T][d_in] and y is [T][d_out].
+ *  - One element type per pool (lora_dtype) for x, W_base, A, B and y.
+ *  - "device" pointers are HIP device memory on the pool's device, 16-byte
+ *    aligned.  The caller owns x, W_base, the index array and y, and keeps them
+ *    alive until the stream work that uses them completes.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the legacy default
+ *    stream.
+ *  - Control-plane calls (create/destroy/quota/register/unregister/policy/
+ *    stats/poll) and lora_apply/lora_route are serialized by a per-pool mutex.
+ *    lora_apply and lora_route share the pool's workspace: calls on
+ *    different streams must be ordered by the caller (one stream per pool is
+ *    the simple contract).
+ */
+#ifndef LORA_H
+#define LORA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- types -- */
+
+typedef struct lora_pool_s *lora_pool; /* opaque; owned by the library */
+
+typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
+
+/* Fused/separate policy.  AUTO: a bucket (the tokens of one adapter in one
+ * call) with more than `threshold` tokens runs FUSED, otherwise SEPARATE
+ * [P4 two-level bucketing].  FUSED / SEPARATE force every bucket. */
+typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_FUSED = 1, LORA_MODE_SEPARATE = 2 } lora_mode;
+
+/* Mode recorded per bucket by routing. */
+#define LORA_SEG_NONE 0     /* base_only or invalid bucket: no LoRA term */
+#define LORA_SEG_FUSED 1    /* LoRA expand added in the base GEMM's epilogue */
+#define LORA_SEG_SEPARATE 2 /* base stored first, LoRA added by a residual kernel */
+
+/* token_adapter_idx value for a token that uses the base model only [P1 三]. */
+#define LORA_BASE_ONLY (-1)
+
+/* Limits of this build. */
+#define LORA_MAX_SLOTS 1024  /* n_slots per pool */
+#define LORA_MAX_RANK 64     /* max_rank per pool */
+
+/* Status codes. */
+#define LORA_OK 0
+#define LORA_EINVAL (-1)      /* null pointer, bad size, slot out of range, misalignment */
+#define LORA_ETOKENS (-2)     /* n_tokens > the pool's max_tokens */
+#define LORA_ESLOT_BUSY (-3)  /* register into a slot that is not FREE */
+#define LORA_ESLOT_EMPTY (-4) /* unregister a slot that holds no adapter */
+#define LORA_ERANK (-5)       /* rank < 1 or rank > the pool's max_rank */
+#define LORA_EALPHA (-6)      /* alpha not finite */
+#define LORA_EQUOTA (-7)      /* tenant's used + slot bytes > its quota [P1 三; P3 accounting] */
+#define LORA_EMISMATCH (-8)   /* shape or dtype does not match the pool's base [P1 三] */
+#define LORA_ENOMEM (-9)      /* device or host allocation failed */
+#define LORA_EHIP (-10)       /* a HIP runtime call failed; lora_strerror has no detail,
+                                 lora_last_hip_error() has the HIP text */
+
+/* Pool statistics.  The `last_*` fields describe the most recent lora_apply
+ * on the pool and are read back from the device (lora_pool_stats
+ * synchronizes).  The three concatenation figures of [P4 zero-pad paragraph]
+ * are: LoRA rows at the padded rank (last_lora_rows_padded), the launch extent
+ * (last_tokens x d_out), and the zero-pad share (last_zero_pad_fraction). */
+typedef struct {
+    int32_t d_in, d_out, max_rank, n_slots, max_tokens, dtype;
+    int32_t active_slots;            /* slots holding a registered adapter */
+    int32_t draining_slots;          /* slots being unregistered */
+    uint64_t slot_bytes;             /* bytes one slot occupies (and is charged) */
+    uint64_t resident_bytes;         /* bytes charged to tenants, all slots */
+    uint64_t device_bytes;           /* device memory the pool holds in total */
+    int32_t last_tokens;
+    int32_t last_adapters;           /* distinct adapters (LoRA buckets) */
+    int32_t last_fused_buckets;
+    int32_t last_separate_buckets;
+    int32_t last_base_only_tokens;
+    int32_t last_invalid_tokens;
+    int64_t last_lora_rows_padded;   /* sum over LoRA tokens of max_rank */
+    int64_t last_lora_rows_true;     /* sum over LoRA tokens of the adapter's rank */
+    double last_zero_pad_fraction;   /* 1 - true / padded (0 if no LoRA token) */
+} lora_stats;
+
+/* ------------------------------------------------------------ lifecycle -- */
+
+/* Create a pool for one linear layer on the current HIP device: n_slots
+ * adapter slots of rank up to max_rank, zero-padded to max_rank [P4 zero-pad],
+ * and a workspace for up to max_tokens tokens per call.  Allocates all device
+ * memory now; lora_apply never allocates.
+ *   d_in, d_out   the base linear's input and output widths.  For LORA_F16 /
+ *                 LORA_BF16 both must be multiples of 64; LORA_F32 takes any.
+ *   max_rank      1..LORA_MAX_RANK;  n_slots 1..LORA_MAX_SLOTS;
+ *   max_tokens    >= 1.
+ * Errors: LORA_EINVAL (bad sizes, out == NULL), LORA_ENOMEM, LORA_EHIP. */
+int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tokens,
+                     lora_dtype dtype, lora_pool *out);
+
+/* Wait for every lora_apply / lora_route enqueued on the pool, then free all
+ * of its device memory and the handle.  p == NULL is a no-op. */
+int lora_pool_destroy(lora_pool p);
+
+/* ------------------------------------------------------- control plane -- */
+
+/* Set a tenant's hard byte quota on this pool [P1 三: vram_quota].  A tenant
+ * whose quota was never set has quota 0: every register is refused (default
+ * deny, [P3 request identity]).  Lowering a quota below the tenant's current
+ * use evicts nothing; later registers are refused.  tenant >= 0. */
+int lora_set_tenant_quota(lora_pool p, int32_t tenant, uint64_t bytes);
+
+/* Register an adapter into a FREE slot [P1 三: validate, then attach].
+ *   A       device, [rank][d_in], pool dtype
+ *   B       device, [d_out][rank], pool dtype
+ *   rank    the adapter's true rank, 1..max_rank; rows/columns rank..max_rank-1
+ *           of the slot are zero-filled [P4 zero-pad]
+ *   alpha   finite; the slot's scale is alpha / rank (the true rank)
+ *   stream  the copies are ordered after earlier work on `stream` (so A and B
+ *           may have been written there) and complete before the call returns;
+ *           A and B may be freed afterwards.
+ * The slot's bytes (lora_stats.slot_bytes) are reserved against the tenant's
+ * quota before anything is copied [P3 accounting]; over quota the call fails
+ * with LORA_EQUOTA and nothing else changes [P1 三: never evict another].
+ * Errors: LORA_EINVAL (slot out of range, NULL A/B, tenant < 0), LORA_ESLOT_BUSY,
+ * LORA_ERANK, LORA_EALPHA, LORA_EQUOTA, LORA_EHIP. */
+int lora_register(lora_pool p, int slot, int32_t tenant, const void *A, const void *B,
+                  int rank, float alpha, void *stream);
+
+/* Unregister by draining [P1 二/三; P3 accounting: never unload weights a
+ * request still holds]: mark the slot DRAINING, wait until every lora_apply
+ * enqueued on the pool before this call has completed, then free the slot
+ * and return its bytes to its tenant.  Blocks the calling thread; applies
+ * from other threads wait on the pool mutex meanwhile.  A token that names
+ * the slot in a later call is invalid (see lora_apply).
+ * Errors: LORA_EINVAL, LORA_ESLOT_EMPTY, LORA_EHIP. */
+int lora_unregister(lora_pool p, int slot);
+
+/* Fused/separate policy [P4 two-level bucketing; SRE item 11].  threshold >= 0
+ * is the bucket size above which AUTO runs FUSED.  Default: AUTO with the
+ * per-device threshold this build ships for gfx950 (lora_get_policy). */
+int lora_set_policy(lora_pool p, lora_mode mode, int threshold);
+int lora_get_policy(lora_pool p, lora_mode *mode, int *threshold);
+
+/* ------------------------------------------------------------ hot path -- */
+
+/* y = x W_base^T + per-token LoRA term, asynchronously on `stream`
+ * [P4 execution unit].  Routing, shrink, base GEMM and expand all run on the
+ * device; the call neither allocates nor synchronizes.
+ *   x                  device, [n_tokens][d_in]
+ *   W_base             device, [d_out][d_in]; never retained by the pool
+ *   token_adapter_idx  device int32 [n_tokens]: a slot, or LORA_BASE_ONLY
+ *   y                  device, [n_tokens][d_out]; must not alias x
+ * A token whose index is neither LORA_BASE_ONLY nor a registered slot (at the
+ * time the call's routing kernel runs) is invalid: its y row is filled with
+ * quiet NaN and the pool's device error counter grows by one; it never falls
+ * back to the base or to another adapter [P3 request identity].
+ * n_tokens == 0 is a no-op.
+ * Errors (host-side, nothing enqueued): LORA_EINVAL, LORA_ETOKENS, LORA_EHIP. */
+int lora_apply(lora_pool p, const void *x, const void *W_base,
+               const int32_t *token_adapter_idx, int n_tokens, void *y, void *stream);
+
+/* Routing alone, asynchronously on `stream` [P4 two-level bucketing]: the
+ * per-token histogram and stable segment sort that lora_apply runs first.
+ * All outputs are device int32 arrays:
+ *   counts[n_slots+2]     tokens per key; key = slot, n_slots = base_only,
+ *                         n_slots+1 = invalid
+ *   offsets[n_slots+3]    exclusive prefix sum of counts
+ *   perm[n_tokens]        perm[p] = token at sorted position p, keys
+ *                         ascending, ties in ascending token order
+ *   segs[(n_slots+2)*4]   {key, start, len, mode} per non-empty key, keys
+ *                         ascending; mode is a LORA_SEG_* value
+ *   n_seg[1]              number of records
+ * Does not touch the error counter.  Errors: LORA_EINVAL, LORA_ETOKENS, LORA_EHIP. */
+int lora_route(lora_pool p, const int32_t *token_adapter_idx, int n_tokens,
+               int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *segs,
+               int32_t *n_seg, void *stream);
+
+/* ---------------------------------------------------------- observation -- */
+
+/* Fill *out (synchronizes with every apply enqueued on the pool). */
+int lora_pool_stats(lora_pool p, lora_stats *out);
+
+/* Bytes currently charged to `tenant` on this pool. */
+int lora_tenant_bytes(lora_pool p, int32_t tenant, uint64_t *out);
+
+/* Read and clear the device count of invalid tokens seen by lora_apply
+ * (synchronizes with every apply enqueued on the pool). */
+int lora_poll_errors(lora_pool p, uint64_t *n_invalid_tokens);
+
+/* Static text for a status code. */
+const char *lora_strerror(int status);
+
+/* Text of the last HIP error seen by this thread inside the library ("" if
+ * none). */
+const char *lora_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_H */

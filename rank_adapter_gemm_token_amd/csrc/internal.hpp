@@ -1,0 +1,98 @@
+// internal.hpp -- device-side records and kernel launchers shared by api.cpp
+// and the .hip kernel files of liblora.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace lora {
+
+// Device slot entry, written by the host at register / unregister time and
+// read by the routing kernel.  state: SLOT_FREE or SLOT_ACTIVE.
+enum : int32_t { SLOT_FREE = 0, SLOT_ACTIVE = 1 };
+struct SlotDev {
+    int32_t state;
+    int32_t rank;   // the adapter's true rank
+    float scale;    // alpha / rank, fp32
+    int32_t pad;
+};
+
+// Statistics of the last routed call, written by the routing kernel.
+struct DevStats {
+    int32_t tokens;
+    int32_t lora_buckets;
+    int32_t fused_buckets;
+    int32_t separate_buckets;
+    int32_t base_only_tokens;
+    int32_t invalid_tokens;
+    int32_t rows_padded;   // sum over LoRA tokens of R
+    int32_t rows_true;     // sum over LoRA tokens of r_i
+};
+
+// Rows per routing tile: LoRA buckets are cut into tiles of this many sorted
+// rows for the shrink and separate-expand kernels.
+constexpr int TILE_ROWS = 16;
+constexpr int MAX_KEYS = 1024 + 2;
+
+// Where routing writes.  The first five arrays are the public routing outputs
+// (lora_route); the rest are internal to lora_apply.
+struct RouteOut {
+    int32_t *counts;    // [S+2]
+    int32_t *offsets;   // [S+3]
+    int32_t *perm;      // [T]   sorted position -> token
+    int32_t *segs;      // [(S+2)*4] {key, start, len, mode}
+    int32_t *n_seg;     // [1]
+    int32_t *pos_seg;   // [T]   sorted position -> bucket record index
+    int32_t *tiles;     // [max_tiles*2] {bucket, first row} of LoRA-bucket tiles
+    int32_t *n_tiles;   // [1]
+    DevStats *stats;    // [1]   may be null
+    unsigned long long *err;  // invalid-token counter, may be null
+};
+
+// Routing inputs and the epilogue's view of it.
+struct RouteView {
+    const int32_t *perm;
+    const int32_t *pos_seg;
+    const int32_t *segs;
+    const int32_t *tiles;
+    const int32_t *n_tiles;
+};
+
+// Upper bound of the number of LoRA-bucket tiles of a T-token call.
+inline int max_tiles(int T, int S) {
+    return (T + TILE_ROWS - 1) / TILE_ROWS + (S < T ? S : T);
+}
+
+// ---- launchers (return the launch's hipError_t) ----
+
+hipError_t launch_route(const int32_t *idx, int T, int S, const SlotDev *slots, int R,
+                        int policy, int theta, const RouteOut &out, hipStream_t st);
+
+// Copy a user adapter into slot `slot` of the slabs, zero-padding rank..R-1.
+// A_user [rank][d_in], B_user [d_out][rank]; slab A [S][R][d_in], slab B
+// [S][d_out][R].  esz = element bytes (2 or 4); the copy is bitwise.
+hipError_t launch_pad_copy(const void *A_user, const void *B_user, void *A_slab, void *B_slab,
+                           int slot, int rank, int R, int d_in, int d_out, int esz,
+                           hipStream_t st);
+
+struct ApplyArgs {
+    int dtype;          // lora_dtype
+    int T, d_in, d_out, S, R;
+    const void *x;      // [T][d_in]
+    const void *W;      // [d_out][d_in]
+    void *y;            // [T][d_out]
+    const void *A_slab; // [S][R][d_in]
+    const void *B_slab; // [S][d_out][R]
+    const SlotDev *slots;
+    float *h;           // [T][R] by sorted position
+    RouteView rv;
+    int tiles_bound;    // grid bound for tile-parallel kernels
+    int policy;         // lora_mode
+};
+
+hipError_t launch_shrink(const ApplyArgs &a, hipStream_t st);
+hipError_t launch_base_gemm(const ApplyArgs &a, hipStream_t st);
+hipError_t launch_expand_separate(const ApplyArgs &a, hipStream_t st);
+
+}  // namespace lora

@@ -1,0 +1,226 @@
+"""Thin ctypes binding of liblora.so (include/lora.h), same names as the C ABI.
+
+Argument marshalling only: tensors become device pointers, streams become raw
+hipStream_t handles, non-zero status codes become LoraError.  Every step of
+the computation runs in liblora.so's HIP kernels; nothing here computes, and
+there is no fallback: importing this module fails if liblora.so is missing.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblora.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError("liblora.so is not built (%s); run `python -m rank_adapter_gemm_token_amd.build` "
+                      "or __graft_entry__.build()" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+
+LORA_F32, LORA_F16, LORA_BF16 = 0, 1, 2
+LORA_MODE_AUTO, LORA_MODE_FUSED, LORA_MODE_SEPARATE = 0, 1, 2
+LORA_SEG_NONE, LORA_SEG_FUSED, LORA_SEG_SEPARATE = 0, 1, 2
+LORA_BASE_ONLY = -1
+LORA_MAX_SLOTS = 1024
+LORA_MAX_RANK = 64
+
+LORA_OK = 0
+LORA_EINVAL = -1
+LORA_ETOKENS = -2
+LORA_ESLOT_BUSY = -3
+LORA_ESLOT_EMPTY = -4
+LORA_ERANK = -5
+LORA_EALPHA = -6
+LORA_EQUOTA = -7
+LORA_EMISMATCH = -8
+LORA_ENOMEM = -9
+LORA_EHIP = -10
+
+DTYPE_OF = {torch.float32: LORA_F32, torch.float16: LORA_F16, torch.bfloat16: LORA_BF16}
+TORCH_DTYPE = {v: k for k, v in DTYPE_OF.items()}
+
+# Every symbol include/lora.h declares, in declaration order.
+EXPORTS = ["lora_pool_create", "lora_pool_destroy", "lora_set_tenant_quota", "lora_register",
+           "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_route",
+           "lora_pool_stats", "lora_tenant_bytes", "lora_poll_errors", "lora_strerror",
+           "lora_last_hip_error"]
+
+
+class lora_stats(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32), ("max_rank", ctypes.c_int32),
+                ("n_slots", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("active_slots", ctypes.c_int32), ("draining_slots", ctypes.c_int32),
+                ("slot_bytes", ctypes.c_uint64), ("resident_bytes", ctypes.c_uint64),
+                ("device_bytes", ctypes.c_uint64),
+                ("last_tokens", ctypes.c_int32), ("last_adapters", ctypes.c_int32),
+                ("last_fused_buckets", ctypes.c_int32), ("last_separate_buckets", ctypes.c_int32),
+                ("last_base_only_tokens", ctypes.c_int32), ("last_invalid_tokens", ctypes.c_int32),
+                ("last_lora_rows_padded", ctypes.c_int64), ("last_lora_rows_true", ctypes.c_int64),
+                ("last_zero_pad_fraction", ctypes.c_double)]
+
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_lib.lora_pool_create.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_vp)]
+_lib.lora_pool_destroy.argtypes = [_vp]
+_lib.lora_set_tenant_quota.argtypes = [_vp, ctypes.c_int32, ctypes.c_uint64]
+_lib.lora_register.argtypes = [_vp, _i, ctypes.c_int32, _vp, _vp, _i, ctypes.c_float, _vp]
+_lib.lora_unregister.argtypes = [_vp, _i]
+_lib.lora_set_policy.argtypes = [_vp, _i, _i]
+_lib.lora_get_policy.argtypes = [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i)]
+_lib.lora_apply.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
+_lib.lora_route.argtypes = [_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.lora_pool_stats.argtypes = [_vp, ctypes.POINTER(lora_stats)]
+_lib.lora_tenant_bytes.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]
+_lib.lora_poll_errors.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
+_lib.lora_strerror.argtypes = [_i]
+_lib.lora_strerror.restype = ctypes.c_char_p
+_lib.lora_last_hip_error.argtypes = []
+_lib.lora_last_hip_error.restype = ctypes.c_char_p
+for _n in EXPORTS:
+    if _n not in ("lora_strerror", "lora_last_hip_error"):
+        getattr(_lib, _n).restype = ctypes.c_int
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        text = lora_strerror(status)
+        if status == LORA_EHIP:
+            text += ": " + _lib.lora_last_hip_error().decode()
+        super().__init__("%s failed: %s (%d)" % (where, text, status))
+
+
+def _check(rc, where):
+    if rc != LORA_OK:
+        raise LoraError(rc, where)
+
+
+def _ptr(t):
+    """Device pointer of a contiguous CUDA tensor (or a raw int / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def lora_strerror(status):
+    return _lib.lora_strerror(int(status)).decode()
+
+
+# Shapes of the pools created through this binding, so that a tensor of the
+# wrong size or dtype is refused here instead of reaching a kernel.
+_shapes = {}
+
+
+def _need(t, numel, dtype, what):
+    if isinstance(t, torch.Tensor):
+        if t.dtype != dtype:
+            raise ValueError("%s: expected %s, got %s" % (what, dtype, t.dtype))
+        if t.numel() < numel:
+            raise ValueError("%s: expected at least %d elements, got %d" % (what, numel, t.numel()))
+
+
+def lora_pool_create(d_in, d_out, max_rank, n_slots, max_tokens, dtype):
+    """Returns the pool handle (an int).  dtype: torch dtype or LORA_F32/F16/BF16."""
+    if isinstance(dtype, torch.dtype):
+        dtype = DTYPE_OF[dtype]
+    h = _vp()
+    _check(_lib.lora_pool_create(d_in, d_out, max_rank, n_slots, max_tokens, int(dtype), ctypes.byref(h)),
+           "lora_pool_create")
+    _shapes[h.value] = dict(d_in=d_in, d_out=d_out, R=max_rank, S=n_slots, max_T=max_tokens,
+                            dtype=TORCH_DTYPE[int(dtype)])
+    return h.value
+
+
+def lora_pool_destroy(pool):
+    _check(_lib.lora_pool_destroy(pool), "lora_pool_destroy")
+    _shapes.pop(pool, None)
+
+
+def lora_set_tenant_quota(pool, tenant, nbytes):
+    _check(_lib.lora_set_tenant_quota(pool, tenant, nbytes), "lora_set_tenant_quota")
+
+
+def lora_register(pool, slot, tenant, A, B, rank, alpha, stream=None):
+    sh = _shapes.get(pool)
+    if sh is not None and 0 < rank:
+        _need(A, rank * sh["d_in"], sh["dtype"], "A")
+        _need(B, sh["d_out"] * rank, sh["dtype"], "B")
+    _check(_lib.lora_register(pool, slot, tenant, _ptr(A), _ptr(B), rank, float(alpha), _stream(stream)),
+           "lora_register")
+
+
+def lora_unregister(pool, slot):
+    _check(_lib.lora_unregister(pool, slot), "lora_unregister")
+
+
+def lora_set_policy(pool, mode, threshold):
+    _check(_lib.lora_set_policy(pool, int(mode), int(threshold)), "lora_set_policy")
+
+
+def lora_get_policy(pool):
+    m, t = _i(), _i()
+    _check(_lib.lora_get_policy(pool, ctypes.byref(m), ctypes.byref(t)), "lora_get_policy")
+    return m.value, t.value
+
+
+def lora_apply(pool, x, W_base, token_adapter_idx, n_tokens, y, stream=None):
+    sh = _shapes.get(pool)
+    if sh is not None and 0 < n_tokens <= sh["max_T"]:
+        _need(x, n_tokens * sh["d_in"], sh["dtype"], "x")
+        _need(W_base, sh["d_out"] * sh["d_in"], sh["dtype"], "W_base")
+        _need(token_adapter_idx, n_tokens, torch.int32, "token_adapter_idx")
+        _need(y, n_tokens * sh["d_out"], sh["dtype"], "y")
+    _check(_lib.lora_apply(pool, _ptr(x), _ptr(W_base), _ptr(token_adapter_idx), int(n_tokens), _ptr(y),
+                           _stream(stream)), "lora_apply")
+
+
+def lora_route(pool, token_adapter_idx, n_tokens, counts, offsets, perm, segs, n_seg, stream=None):
+    sh = _shapes.get(pool)
+    if sh is not None and 0 <= n_tokens <= sh["max_T"]:
+        S = sh["S"]
+        _need(token_adapter_idx, n_tokens, torch.int32, "token_adapter_idx")
+        _need(counts, S + 2, torch.int32, "counts")
+        _need(offsets, S + 3, torch.int32, "offsets")
+        _need(perm, n_tokens, torch.int32, "perm")
+        _need(segs, (S + 2) * 4, torch.int32, "segs")
+        _need(n_seg, 1, torch.int32, "n_seg")
+    _check(_lib.lora_route(pool, _ptr(token_adapter_idx), int(n_tokens), _ptr(counts), _ptr(offsets),
+                           _ptr(perm), _ptr(segs), _ptr(n_seg), _stream(stream)), "lora_route")
+
+
+def lora_pool_stats(pool):
+    s = lora_stats()
+    _check(_lib.lora_pool_stats(pool, ctypes.byref(s)), "lora_pool_stats")
+    return {name: getattr(s, name) for name, _ in lora_stats._fields_}
+
+
+def lora_tenant_bytes(pool, tenant):
+    v = ctypes.c_uint64()
+    _check(_lib.lora_tenant_bytes(pool, tenant, ctypes.byref(v)), "lora_tenant_bytes")
+    return v.value
+
+
+def lora_poll_errors(pool):
+    v = ctypes.c_uint64()
+    _check(_lib.lora_poll_errors(pool, ctypes.byref(v)), "lora_poll_errors")
+    return v.value
+
+
+def raw_lib():
+    """The loaded CDLL, for tests that call the C ABI directly."""
+    return _lib

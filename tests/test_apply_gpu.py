@@ -1,0 +1,98 @@
+"""lora_apply on the GPU (through the C ABI) vs the CPU fp64 oracle, on the five
+workloads and on small ragged shapes, under every fused/separate policy."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import Pool, assert_close, dev, reference, sample_rows
+from rank_adapter_gemm_token_amd import lora
+from rank_adapter_gemm_token_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+POLICIES = [(lora.LORA_MODE_AUTO, 16), (lora.LORA_MODE_FUSED, 16), (lora.LORA_MODE_SEPARATE, 16),
+            (lora.LORA_MODE_AUTO, 0), (lora.LORA_MODE_AUTO, 3)]
+
+
+def _run_full(w, lin, policy, theta, rows=None):
+    p = Pool(lin.d_in, lin.d_out, w.R, w.S, w.T, w.dtype, policy, theta)
+    try:
+        p.register_all(lin.adapters)
+        x, W, idx = dev(w.x[lin.d_in]), dev(lin.W), dev(w.idx)
+        y = p.apply(x, W, idx)
+        torch.cuda.synchronize()
+        y_ref, inv = reference(p, w.x[lin.d_in], lin.W, w.idx, rows=rows)
+        got = y.cpu() if rows is None else y.cpu()[torch.as_tensor(rows)]
+        return assert_close(got, y_ref, inv, w.dtype)
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("policy,theta", POLICIES)
+def test_tiny_fp32_full(policy, theta):
+    w = wl.tiny()
+    _run_full(w, w.linears[0], policy, theta)
+
+
+@pytest.mark.parametrize("policy,theta", POLICIES[:3])
+def test_decode_fp16_full(policy, theta):
+    w = wl.decode()
+    _run_full(w, w.linears[0], policy, theta)
+
+
+@pytest.mark.parametrize("T", wl.SWEEP_T)
+def test_sweep_fp16_full(T):
+    w = wl.sweep(T)
+    _run_full(w, w.linears[0], lora.LORA_MODE_AUTO, 16)
+
+
+@pytest.mark.parametrize("proj", [0, 1])
+def test_prefill_bf16_sampled(proj):
+    w = wl.prefill()
+    ends = [s * 512 for s in range(8)] + [s * 512 + 511 for s in range(8)]
+    rows = sample_rows(w.T, 48, seed=proj, must=ends)
+    _run_full(w, w.linears[proj], lora.LORA_MODE_AUTO, 16, rows=rows)
+
+
+@pytest.mark.parametrize("layer,proj", [(0, p) for p in range(7)] + [(31, 6)])
+def test_stack_bf16_sampled(layer, proj):
+    idx = wl.stack_idx()
+    lin = wl.stack_linear(layer, proj, "cuda")
+    x = wl.stack_x(lin.d_in, device="cpu")
+    w = wl.Workload("stack", "bf16", 256, 64, 16, idx, {lin.d_in: x}, [lin], 5)
+    rows = sample_rows(256, 24, seed=layer * 7 + proj)
+    _run_full(w, lin, lora.LORA_MODE_AUTO, 16, rows=rows)
+
+
+def _small_case(dtype, T, d_in, d_out, S, R, seed):
+    rng = np.random.default_rng(seed)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    x = torch.from_numpy(rng.standard_normal((T, d_in))).to(tdt)
+    W = torch.from_numpy(rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).to(tdt)
+    ads = []
+    for s in range(S):
+        r = int(rng.integers(1, R + 1))
+        ads.append(wl.Adapter(s, s, r, float(2 * r),
+                              torch.from_numpy(rng.standard_normal((r, d_in)) / np.sqrt(d_in)).to(tdt),
+                              torch.from_numpy(rng.standard_normal((d_out, r)) * 0.1).to(tdt)))
+    idx = torch.from_numpy(rng.integers(-1, S + 2, size=T).astype(np.int32))  # incl. invalid
+    return x, W, ads, idx
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("T,d_in,d_out,S,R", [(1, 64, 64, 1, 1), (37, 128, 192, 5, 8),
+                                               (77, 192, 128, 9, 16), (300, 256, 320, 17, 64),
+                                               (513, 64, 128, 40, 24)])
+@pytest.mark.parametrize("policy", [0, 1, 2])
+def test_small_ragged_full(dtype, T, d_in, d_out, S, R, policy):
+    x, W, ads, idx = _small_case(dtype, T, d_in, d_out, S, R, seed=T * 31 + S)
+    p = Pool(d_in, d_out, R, S, T, dtype, policy, 4)
+    try:
+        p.register_all(ads)
+        y = p.apply(dev(x), dev(W), dev(idx))
+        torch.cuda.synchronize()
+        y_ref, inv = reference(p, x, W, idx)
+        assert_close(y.cpu(), y_ref, inv, dtype)
+        assert p.poll_errors() == int(inv.sum())
+    finally:
+        p.close()

@@ -1,0 +1,111 @@
+"""Host-side checks that need no GPU: the C-ABI library loads and exports every
+symbol include/lora.h declares, argument validation that fails before any
+device call, the public struct layout, and the slot book / tenant ledger
+(compiled on its own with g++)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+
+def _lora():
+    from rank_adapter_gemm_token_amd import lora
+    return lora
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(_lora().EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lora().raw_lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lora().LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (lora_\w+)", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_library_has_gfx950_code():
+    out = subprocess.run(["/opt/rocm/llvm/bin/llvm-readelf", "-S", _lora().LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    assert ".hip_fatbin" in out
+    blob = open(_lora().LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_strerror_texts():
+    L = _lora()
+    codes = [L.LORA_OK, L.LORA_EINVAL, L.LORA_ETOKENS, L.LORA_ESLOT_BUSY, L.LORA_ESLOT_EMPTY,
+             L.LORA_ERANK, L.LORA_EALPHA, L.LORA_EQUOTA, L.LORA_EMISMATCH, L.LORA_ENOMEM, L.LORA_EHIP]
+    texts = [L.lora_strerror(c) for c in codes]
+    assert len(set(texts)) == len(texts)
+    assert L.lora_strerror(-999) == "unknown status"
+
+
+def test_validation_before_device_use():
+    lib = _lora().raw_lib()
+    L = _lora()
+    h = ctypes.c_void_p()
+    # Bad sizes / dtype / null output: refused before touching the device.
+    assert lib.lora_pool_create(0, 64, 8, 4, 16, 1, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_pool_create(64, 64, 0, 4, 16, 1, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_pool_create(64, 64, 65, 4, 16, 1, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_pool_create(64, 64, 8, 0, 16, 1, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_pool_create(64, 64, 8, 1025, 16, 1, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_pool_create(64, 64, 8, 4, 0, 1, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_pool_create(64, 64, 8, 4, 16, 7, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_pool_create(96, 64, 8, 4, 16, 1, ctypes.byref(h)) == L.LORA_EINVAL  # fp16 needs %64
+    assert lib.lora_pool_create(64, 64, 8, 4, 16, 1, None) == L.LORA_EINVAL
+    # Null pool handles.
+    assert lib.lora_pool_destroy(None) == L.LORA_OK
+    assert lib.lora_apply(None, None, None, None, 4, None, None) == L.LORA_EINVAL
+    assert lib.lora_register(None, 0, 0, None, None, 8, ctypes.c_float(16.0), None) == L.LORA_EINVAL
+    assert lib.lora_unregister(None, 0) == L.LORA_EINVAL
+    assert lib.lora_set_tenant_quota(None, 0, 10) == L.LORA_EINVAL
+    assert lib.lora_set_policy(None, 0, 16) == L.LORA_EINVAL
+    assert lib.lora_route(None, None, 0, None, None, None, None, None, None) == L.LORA_EINVAL
+    s = L.lora_stats()
+    assert lib.lora_pool_stats(None, ctypes.byref(s)) == L.LORA_EINVAL
+    v = ctypes.c_uint64()
+    assert lib.lora_poll_errors(None, ctypes.byref(v)) == L.LORA_EINVAL
+    assert lib.lora_tenant_bytes(None, 0, ctypes.byref(v)) == L.LORA_EINVAL
+
+
+def test_stats_struct_layout_matches_header(tmp_path):
+    L = _lora()
+    fields = [n for n, _ in L.lora_stats._fields_]
+    src = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "lora.h"', 'int main(void){',
+             'printf("%zu\\n", sizeof(lora_stats));']
+    lines += ['printf("%%zu\\n", offsetof(lora_stats, %s));' % f for f in fields]
+    lines += ['return 0;}']
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(L.lora_stats)
+    assert got[1:] == [getattr(L.lora_stats, f).offset for f in fields]
+
+
+def test_slot_book_and_ledger(tmp_path):
+    exe = tmp_path / "ledger_check"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-o", str(exe),
+                    os.path.join(ROOT, "tests", "native", "ledger_check.cpp"),
+                    os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc", "ledger.cpp")],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
