@@ -1,0 +1,328 @@
+"""Throughput of the multi-LoRA adapter execution unit on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+Default workload: decode-shaped q_proj, 4096x4096 fp16 base, 6 adapters of
+rank 16 (alpha 32) in an HBM pool, 64 tokens per call with 10% base_only.  A
+step is one lora_apply over one batch: routing, shrink, base GEMM with the
+fused expand, separate expand.  Inputs are resident in HBM before timing.
+To keep the 256 MB last-level cache from serving the 32 MiB base weight,
+steps rotate over 16 independent (W, pool, x, idx, y) copies (>= 512 MiB).
+
+Prints ONE JSON line: tokens/s over K timed steps (HIP events on the stream
+the kernels run on, synchronize on both sides), the roofline of the dominant
+kernel (its algorithmic bytes over its average duration, timed with per-stage
+HIP events in a second pass of K steps), and the CPU fp64 oracle timed on the
+host cores on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "multi-LoRA linear tokens/s + % HBM/MFMA roofline, 4096² r=16, batch 1–256"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+ESZ = {"f32": 4, "f16": 2, "bf16": 2}
+TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+KERNEL_SOURCE = os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc", "apply_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# workload set-up (inputs drawn by the seeded generators, then made resident)
+# ----------------------------------------------------------------------------
+
+class Call:
+    """One lora_apply of a step, with its algorithmic figures."""
+
+    def __init__(self, pool, x, W, idx, y, T, d_in, d_out, dtype, distinct, ranks, fused_slots):
+        self.pool, self.x, self.W, self.idx, self.y = pool, x, W, idx, y
+        e = ESZ[dtype]
+        self.T, self.d_in, self.d_out = T, d_in, d_out
+        r_sum = sum(ranks[s] for s in distinct)
+        r_fused = sum(ranks[s] for s in fused_slots)
+        # Whole call: W once, x once, y once, A and B of each distinct adapter
+        # touched (true rank) once, plus the index array.
+        self.call_bytes = d_in * d_out * e + T * (d_in + d_out) * e + r_sum * (d_in + d_out) * e + 4 * T
+        # Base GEMM kernel (with the fused expand): W, x, y, B of fused buckets.
+        self.gemm_bytes = d_in * d_out * e + T * (d_in + d_out) * e + r_fused * d_out * e
+        lora_tokens = int(sum(1 for v in idx.cpu().tolist() if v in ranks))
+        self.call_flops = 2 * T * d_in * d_out + 2 * sum(
+            ranks.get(int(v), 0) for v in idx.cpu().tolist()) * (d_in + d_out)
+        self.gemm_flops = 2 * T * d_in * d_out
+        self.lora_tokens = lora_tokens
+
+
+def _register(L, pool, lin, stream=None):
+    for a in lin.adapters:
+        L.lora_set_tenant_quota(pool, a.tenant, 1 << 50)
+        L.lora_register(pool, a.slot, a.tenant, a.A.cuda(), a.B.cuda(), a.rank, a.alpha)
+
+
+def _buckets(idx_cpu, ranks, policy, theta):
+    vals, counts = np.unique(idx_cpu.numpy(), return_counts=True)
+    distinct = [int(v) for v in vals if int(v) in ranks]
+    fused = []
+    for v, c in zip(vals, counts):
+        v = int(v)
+        if v in ranks and (policy == 1 or (policy == 0 and c > theta)):
+            fused.append(v)
+    return distinct, fused
+
+
+def build_linear_copies(L, w, lin, copies, policy, theta):
+    """`copies` independent (pool, W, x, idx, y) sets for one linear."""
+    out = []
+    ranks = {a.slot: a.rank for a in lin.adapters}
+    distinct, fused = _buckets(w.idx, ranks, policy, theta)
+    for c in range(copies):
+        pool = L.lora_pool_create(lin.d_in, lin.d_out, w.R, w.S, w.T, TDT[w.dtype])
+        L.lora_set_policy(pool, policy, theta)
+        _register(L, pool, lin)
+        x = w.x[lin.d_in].cuda().contiguous()
+        W = lin.W.cuda().contiguous() if c == 0 else out[0].W.clone()
+        idx = w.idx.cuda().contiguous()
+        y = torch.empty((w.T, lin.d_out), dtype=TDT[w.dtype], device="cuda")
+        out.append(Call(pool, x, W, idx, y, w.T, lin.d_in, lin.d_out, w.dtype, distinct, ranks, fused))
+    return out
+
+
+def setup(args, L):
+    from rank_adapter_gemm_token_amd import workloads as wl
+    if args.workload == "decode":
+        w = wl.decode()
+        calls = build_linear_copies(L, w, w.linears[0], args.copies, args.policy, args.theta)
+        steps = [[c] for c in calls]
+        desc = ("decode q_proj 4096x4096 fp16, 6 adapters r16 alpha32 in an HBM pool, "
+                "64 tokens (10% base_only)")
+    elif args.workload.startswith("sweep"):
+        T = int(args.workload[len("sweep"):] or 64)
+        w = wl.sweep(T)
+        calls = build_linear_copies(L, w, w.linears[0], args.copies, args.policy, args.theta)
+        steps = [[c] for c in calls]
+        desc = "sweep 4096x4096 fp16, 100 adapters r8 alpha16, %d tokens, Zipf(1.1)" % T
+    elif args.workload == "prefill":
+        w = wl.prefill()
+        per = [build_linear_copies(L, w, lin, max(1, args.copies // 4), args.policy, args.theta)
+               for lin in w.linears]
+        steps = [list(s) for s in zip(*per)]
+        desc = ("prefill q_proj+v_proj 4096x4096 bf16, 32 adapters r{8,16,32,64} padded to 64, "
+                "8 sequences x 512 tokens")
+    elif args.workload == "stack":
+        w = wl.stack(layers=args.layers)
+        step = []
+        for lin in w.linears:
+            step += build_linear_copies(L, w, lin, 1, args.policy, args.theta)
+            lin.W = None
+            for a in lin.adapters:
+                a.A = a.B = None
+        steps = [step]
+        desc = ("stack: %d layers x {q,k,v,o 4096x4096; gate,up 4096x11008; down 11008x4096} bf16, "
+                "64 adapters r16 alpha32, 256 tokens (Zipf 1.1 + 5%% base_only)" % args.layers)
+    else:
+        raise SystemExit("unknown workload " + args.workload)
+    return w, steps, desc
+
+
+# ----------------------------------------------------------------------------
+# timing
+# ----------------------------------------------------------------------------
+
+def run_steps(L, steps, n, start=0):
+    for i in range(start, start + n):
+        for c in steps[i % len(steps)]:
+            L.lora_apply(c.pool, c.x, c.W, c.idx, c.T, c.y)
+
+
+def timed(L, steps, K):
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    run_steps(L, steps, K)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / 1e3
+
+
+def stage_profile(L, steps, K):
+    pools = sorted({c.pool for s in steps for c in s})
+    per_pool = {}
+    for s in steps:
+        for c in s:
+            per_pool[c.pool] = per_pool.get(c.pool, 0) + 1
+    for p in pools:
+        L.lora_profile_enable(p, 1, per_pool[p] * (K // len(steps) + 2))
+    torch.cuda.synchronize()
+    run_steps(L, steps, K)
+    torch.cuda.synchronize()
+    tot = {"calls": 0, "route_ms": 0.0, "shrink_ms": 0.0, "gemm_ms": 0.0, "expand_ms": 0.0}
+    for p in pools:
+        r = L.lora_profile_read(p)
+        for k in tot:
+            tot[k] += r[k]
+        L.lora_profile_enable(p, 0)
+    return tot
+
+
+def kernel_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload_key):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload_key)
+    if not ent or ent.get("kernel_sha") != kernel_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on host cores, bounded sample of the same workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(w, seconds):
+    import oracle
+    lin = w.linears[0]
+    cores = len(os.sched_getaffinity(0))
+    x = oracle.to_f64(w.x[lin.d_in])
+    W = oracle.to_f64(lin.W)
+    idx = w.idx.numpy()
+    ads = {a.slot: (oracle.to_f64(a.A), oracle.to_f64(a.B), a.rank, a.alpha) for a in lin.adapters}
+    oracle.apply(x[:1], W, idx[:1], w.S, ads, n_threads=cores)  # load + first touch
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.apply(x, W, idx, w.S, ads, n_threads=cores)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": w.T * reps / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d full calls of the %s linear (%d tokens each, fp64, %.1f s)"
+                      % (reps, lin.name, w.T, el)}
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="decode",
+                    help="decode (default) | sweep<T> | prefill | stack")
+    ap.add_argument("--copies", type=int, default=16)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--policy", type=int, default=0, help="0 auto, 1 fused, 2 separate")
+    ap.add_argument("--theta", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-stage pass")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    from rank_adapter_gemm_token_amd import lora as L
+    if args.theta is None:
+        args.theta = 16
+
+    w, steps, desc = setup(args, L)
+    log("workload:", desc, "| step sets:", len(steps), "| calls/step:", len(steps[0]))
+    run_steps(L, steps, args.warmup)
+    torch.cuda.synchronize()
+    sec = timed(L, steps, args.steps)
+    tokens_per_step = w.T
+    value = tokens_per_step * args.steps / sec
+    ms_per_step = sec * 1e3 / args.steps
+    log("timed: %.3f ms/step, %.0f tokens/s" % (ms_per_step, value))
+
+    calls = steps[0]
+    step_bytes = sum(c.call_bytes for c in calls)
+    step_flops = sum(c.call_flops for c in calls)
+    mfma_bound = args.workload == "prefill"
+    roof = None
+    stages = None
+    if not args.no_profile:
+        prof = stage_profile(L, steps, args.steps)
+        n = prof["calls"]
+        stages = {k: prof[k] / n for k in ("route_ms", "shrink_ms", "gemm_ms", "expand_ms")}
+        log("per-call stage ms (events):", {k: round(v * 1e3, 2) for k, v in stages.items()}, "us")
+        calls_per_step = len(calls)
+        gemm_s = stages["gemm_ms"] / 1e3
+        if mfma_bound:
+            achieved = (sum(c.gemm_flops for c in calls) / calls_per_step) / gemm_s / 1e12
+            roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS[w.dtype]}
+        else:
+            per_launch = sum(c.gemm_bytes for c in calls) / calls_per_step
+            achieved = per_launch / gemm_s / 1e9
+            roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS}
+        roof["kernel"] = "k_gemm_mfma (base GEMM + fused expand)"
+        roof["traffic"] = traffic_for(args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline and (args.workload == "decode" or args.workload.startswith("sweep")):
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log("cpu baseline:", cpu)
+
+    step_s = sec / args.steps
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded generators; 7B-decoder shapes, N(0,1) x, N(0,1/d_in) W and A, "
+                "N(0,0.01) B)",
+        "config": {"workload": desc, "tokens_per_step": tokens_per_step,
+                   "calls_per_step": len(calls), "weight_copies": len(steps),
+                   "policy": ["auto", "fused", "separate"][args.policy], "theta": args.theta,
+                   "step_bytes_alg": step_bytes, "step_flops_alg": step_flops},
+        "step_roofline": {"hbm_GBs": step_bytes / step_s / 1e9,
+                          "hbm_frac": step_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+                          "mfma_TFLOPs": step_flops / step_s / 1e12,
+                          "mfma_frac": step_flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]},
+        "roofline": roof,
+        "stage_us_per_call": None if stages is None else {k.replace("_ms", ""): v * 1e3
+                                                          for k, v in stages.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -222,6 +222,25 @@ int lora_tenant_bytes(lora_pool p, int32_t tenant, uint64_t *out);
  * (synchronizes with every apply enqueued on the pool). */
 int lora_poll_errors(lora_pool p, uint64_t *n_invalid_tokens);
 
+/* Per-stage device time of lora_apply, for measurement.  When enabled, each
+ * lora_apply (up to max_calls of them between two reads) records HIP timing
+ * events on its own stream before routing and after the routing, shrink,
+ * base-GEMM and separate-expand launches; a stage's time is the interval
+ * between its two events.  Events are created by lora_profile_enable, not on
+ * the hot path.  enable = 0 turns it off and frees the events. */
+typedef struct {
+    int64_t calls;      /* timed lora_apply calls since the last read */
+    double route_ms;    /* summed over those calls */
+    double shrink_ms;
+    double gemm_ms;     /* base projection, including the fused expand */
+    double expand_ms;   /* separate residual expand */
+} lora_profile;
+
+int lora_profile_enable(lora_pool p, int enable, int max_calls);
+
+/* Synchronize with the timed calls, fill *out and start a new interval. */
+int lora_profile_read(lora_pool p, lora_profile *out);
+
 /* Static text for a status code. */
 const char *lora_strerror(int status);
 

@@ -85,12 +85,28 @@ struct lora_pool_s {
     int policy = LORA_MODE_AUTO;
     int theta = kDefaultTheta;
 
+    // Opt-in stage timing (lora_profile_enable).
+    struct ProfSet {
+        hipEvent_t e[5];
+    };
+    std::vector<ProfSet> prof;
+    size_t prof_used = 0;
+
     lora_pool_s(int n_slots, int max_rank, uint64_t slot_bytes) : book(n_slots, max_rank, slot_bytes) {}
 };
 
 namespace {
 
+void free_profile(lora_pool p) {
+    for (auto &ps : p->prof)
+        for (hipEvent_t e : ps.e)
+            if (e) (void)hipEventDestroy(e);
+    p->prof.clear();
+    p->prof_used = 0;
+}
+
 void free_pool_memory(lora_pool p) {
+    free_profile(p);
     if (p->A_slab) (void)hipFree(p->A_slab);
     if (p->B_slab) (void)hipFree(p->B_slab);
     if (p->slots_dev) (void)hipFree(p->slots_dev);
@@ -338,9 +354,13 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     DeviceGuard g(p->device);
     HIP_TRY(g.error());
     hipStream_t st = static_cast<hipStream_t>(stream);
+    lora_pool_s::ProfSet *ps = (p->prof_used < p->prof.size()) ? &p->prof[p->prof_used++] : nullptr;
+    auto mark = [&](int i) { return ps ? hipEventRecord(ps->e[i], st) : hipSuccess; };
 
+    HIP_TRY(mark(0));
     HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
                                p->ro, st));
+    HIP_TRY(mark(1));
     lora::ApplyArgs a{};
     a.dtype = p->dtype;
     a.T = n_tokens;
@@ -359,8 +379,11 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     a.tiles_bound = lora::max_tiles(n_tokens, p->S);
     a.policy = p->policy;
     HIP_TRY(lora::launch_shrink(a, st));
+    HIP_TRY(mark(2));
     HIP_TRY(lora::launch_base_gemm(a, st));
+    HIP_TRY(mark(3));
     if (p->policy != LORA_MODE_FUSED) HIP_TRY(lora::launch_expand_separate(a, st));
+    HIP_TRY(mark(4));
     HIP_TRY(record_inflight(p, st));
     return LORA_OK;
 }
@@ -441,6 +464,54 @@ int lora_poll_errors(lora_pool p, uint64_t *n_invalid_tokens) {
     HIP_TRY(hipMemcpyAsync(p->ro.err, &zero, sizeof zero, hipMemcpyHostToDevice, p->internal));
     HIP_TRY(hipStreamSynchronize(p->internal));
     *n_invalid_tokens = v;
+    return LORA_OK;
+}
+
+int lora_profile_enable(lora_pool p, int enable, int max_calls) {
+    if (p == nullptr || (enable && max_calls < 1)) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(p->mu);
+    DeviceGuard g(p->device);
+    HIP_TRY(g.error());
+    HIP_TRY(drain_inflight(p));
+    free_profile(p);
+    if (!enable) return LORA_OK;
+    try {
+        p->prof.resize(static_cast<size_t>(max_calls));
+    } catch (...) {
+        return LORA_ENOMEM;
+    }
+    for (auto &ps : p->prof)
+        for (hipEvent_t &e : ps.e) e = nullptr;
+    for (auto &ps : p->prof) {
+        for (hipEvent_t &e : ps.e) {
+            hipError_t err = hipEventCreate(&e);
+            if (err != hipSuccess) {
+                free_profile(p);
+                return hip_fail(err);
+            }
+        }
+    }
+    return LORA_OK;
+}
+
+int lora_profile_read(lora_pool p, lora_profile *out) {
+    if (p == nullptr || out == nullptr) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(p->mu);
+    DeviceGuard g(p->device);
+    HIP_TRY(g.error());
+    std::memset(out, 0, sizeof *out);
+    double *acc[4] = {&out->route_ms, &out->shrink_ms, &out->gemm_ms, &out->expand_ms};
+    for (size_t c = 0; c < p->prof_used; ++c) {
+        lora_pool_s::ProfSet &ps = p->prof[c];
+        HIP_TRY(hipEventSynchronize(ps.e[4]));
+        for (int i = 0; i < 4; ++i) {
+            float ms = 0.0f;
+            HIP_TRY(hipEventElapsedTime(&ms, ps.e[i], ps.e[i + 1]));
+            *acc[i] += ms;
+        }
+    }
+    out->calls = static_cast<int64_t>(p->prof_used);
+    p->prof_used = 0;
     return LORA_OK;
 }
 

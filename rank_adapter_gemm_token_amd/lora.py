@@ -42,8 +42,8 @@ TORCH_DTYPE = {v: k for k, v in DTYPE_OF.items()}
 # Every symbol include/lora.h declares, in declaration order.
 EXPORTS = ["lora_pool_create", "lora_pool_destroy", "lora_set_tenant_quota", "lora_register",
            "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_route",
-           "lora_pool_stats", "lora_tenant_bytes", "lora_poll_errors", "lora_strerror",
-           "lora_last_hip_error"]
+           "lora_pool_stats", "lora_tenant_bytes", "lora_poll_errors", "lora_profile_enable",
+           "lora_profile_read", "lora_strerror", "lora_last_hip_error"]
 
 
 class lora_stats(ctypes.Structure):
@@ -57,6 +57,11 @@ class lora_stats(ctypes.Structure):
                 ("last_base_only_tokens", ctypes.c_int32), ("last_invalid_tokens", ctypes.c_int32),
                 ("last_lora_rows_padded", ctypes.c_int64), ("last_lora_rows_true", ctypes.c_int64),
                 ("last_zero_pad_fraction", ctypes.c_double)]
+
+
+class lora_profile(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int64), ("route_ms", ctypes.c_double), ("shrink_ms", ctypes.c_double),
+                ("gemm_ms", ctypes.c_double), ("expand_ms", ctypes.c_double)]
 
 
 _vp = ctypes.c_void_p
@@ -73,6 +78,8 @@ _lib.lora_route.argtypes = [_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.lora_pool_stats.argtypes = [_vp, ctypes.POINTER(lora_stats)]
 _lib.lora_tenant_bytes.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]
 _lib.lora_poll_errors.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
+_lib.lora_profile_enable.argtypes = [_vp, _i, _i]
+_lib.lora_profile_read.argtypes = [_vp, ctypes.POINTER(lora_profile)]
 _lib.lora_strerror.argtypes = [_i]
 _lib.lora_strerror.restype = ctypes.c_char_p
 _lib.lora_last_hip_error.argtypes = []
@@ -219,6 +226,16 @@ def lora_poll_errors(pool):
     v = ctypes.c_uint64()
     _check(_lib.lora_poll_errors(pool, ctypes.byref(v)), "lora_poll_errors")
     return v.value
+
+
+def lora_profile_enable(pool, enable, max_calls=1):
+    _check(_lib.lora_profile_enable(pool, int(bool(enable)), int(max_calls)), "lora_profile_enable")
+
+
+def lora_profile_read(pool):
+    v = lora_profile()
+    _check(_lib.lora_profile_read(pool, ctypes.byref(v)), "lora_profile_read")
+    return {name: getattr(v, name) for name, _ in lora_profile._fields_}
 
 
 def raw_lib():
