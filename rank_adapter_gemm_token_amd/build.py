@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "liblora.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "ledger.cpp", "route.hip", "pad_copy.hip", "apply_kernels.hip"]
+SOURCES = ["api.cpp", "ledger.cpp", "route.hip", "pad_copy.hip", "apply_kernels.hip", "gemm_decode.hip",
+           "shrink_expand.hip"]
 
 # Packed-fp32 VALU instructions are kept out of every device object.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -29,6 +30,8 @@ CXXFLAGS = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=" + ARCH, "-Wall",
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *CXXFLAGS, *DEVICE_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    if os.environ.get("LORA_RESOURCE_USAGE"):
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

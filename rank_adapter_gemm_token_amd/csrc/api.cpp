@@ -66,6 +66,7 @@ constexpr int kDefaultTheta = 16;
 struct lora_pool_s {
     int device = 0;
     int d_in = 0, d_out = 0, R = 0, S = 0, max_T = 0;
+    int Rp = 0;  // slab rank: R rounded up to a multiple of 8 (16-byte rows of B)
     lora_dtype dtype = LORA_F32;
     int esz = 4;
     lora::SlotBook book;
@@ -78,6 +79,7 @@ struct lora_pool_s {
 
     lora::RouteOut ro{};
     float *h = nullptr;
+    void *gpart = nullptr;
 
     hipStream_t internal = nullptr;
     std::mutex mu;
@@ -182,12 +184,14 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     }
     if (esz == 2 && (d_in % 64 != 0 || d_out % 64 != 0)) return LORA_EINVAL;
 
-    const uint64_t slot_bytes = static_cast<uint64_t>(max_rank) * (d_in + d_out) * esz;
+    const int Rp = (max_rank + 7) / 8 * 8;
+    const uint64_t slot_bytes = static_cast<uint64_t>(Rp) * (d_in + d_out) * esz;
     lora_pool p = new (std::nothrow) lora_pool_s(n_slots, max_rank, slot_bytes);
     if (p == nullptr) return LORA_ENOMEM;
     p->d_in = d_in;
     p->d_out = d_out;
     p->R = max_rank;
+    p->Rp = Rp;
     p->S = n_slots;
     p->max_T = max_tokens;
     p->dtype = dtype;
@@ -203,8 +207,9 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
 
     const size_t S = static_cast<size_t>(n_slots);
     const size_t T = static_cast<size_t>(max_tokens);
-    const size_t a_bytes = S * max_rank * d_in * esz;
-    const size_t b_bytes = S * d_out * max_rank * esz;
+    const size_t a_bytes = S * Rp * d_in * esz;
+    const size_t b_bytes = S * d_out * Rp * esz;
+    const size_t dec_T = static_cast<size_t>(max_tokens < lora::DECODE_MAX_T ? max_tokens : lora::DECODE_MAX_T);
 
     // Workspace layout, each piece 256-byte aligned.
     size_t off = 0;
@@ -219,11 +224,18 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     const size_t o_segs = take((S + 2) * 16);
     const size_t o_nseg = take(4);
     const size_t o_posseg = take(T * 4);
+    const size_t o_tokpos = take(T * 4);
+    const size_t o_tokseg = take(T * 4);
     const size_t o_tiles = take(static_cast<size_t>(lora::max_tiles(max_tokens, n_slots)) * 8);
     const size_t o_ntiles = take(4);
     const size_t o_stats = take(sizeof(lora::DevStats));
     const size_t o_err = take(8);
-    const size_t o_h = take(T * max_rank * 4);
+    // h: up to 8 k parts of [T][Rp] fp32 (the decode shrink's parts).
+    const size_t o_h = take(8 * T * Rp * 4);
+    // Split-K partial sums of the decode GEMM: splits x d_out x T_pad fp32.
+    const size_t o_gpart = take(esz == 2 ? static_cast<size_t>(lora::decode_splits(static_cast<int>(dec_T), d_in, d_out)) *
+                                               16 * lora::decode_token_blocks(static_cast<int>(dec_T)) * d_out * 4
+                                         : 0);
     const size_t ws_bytes = off;
 
     e = hipMalloc(&p->A_slab, a_bytes);
@@ -249,11 +261,14 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     p->ro.segs = reinterpret_cast<int32_t *>(w + o_segs);
     p->ro.n_seg = reinterpret_cast<int32_t *>(w + o_nseg);
     p->ro.pos_seg = reinterpret_cast<int32_t *>(w + o_posseg);
+    p->ro.tok_pos = reinterpret_cast<int32_t *>(w + o_tokpos);
+    p->ro.tok_seg = reinterpret_cast<int32_t *>(w + o_tokseg);
     p->ro.tiles = reinterpret_cast<int32_t *>(w + o_tiles);
     p->ro.n_tiles = reinterpret_cast<int32_t *>(w + o_ntiles);
     p->ro.stats = reinterpret_cast<lora::DevStats *>(w + o_stats);
     p->ro.err = reinterpret_cast<unsigned long long *>(w + o_err);
     p->h = reinterpret_cast<float *>(w + o_h);
+    p->gpart = w + o_gpart;
     *out = p;
     return LORA_OK;
 }
@@ -288,7 +303,7 @@ int lora_register(lora_pool p, int slot, int32_t tenant, const void *A, const vo
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = g.error();
     if (e == hipSuccess)
-        e = lora::launch_pad_copy(A, B, p->A_slab, p->B_slab, slot, rank, p->R, p->d_in, p->d_out, p->esz, st);
+        e = lora::launch_pad_copy(A, B, p->A_slab, p->B_slab, slot, rank, p->Rp, p->d_in, p->d_out, p->esz, st);
     lora::SlotDev ent{lora::SLOT_ACTIVE, rank, alpha / static_cast<float>(rank), 0};
     if (e == hipSuccess)
         e = hipMemcpyAsync(p->slots_dev + slot, &ent, sizeof ent, hipMemcpyHostToDevice, st);
@@ -367,7 +382,7 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     a.d_in = p->d_in;
     a.d_out = p->d_out;
     a.S = p->S;
-    a.R = p->R;
+    a.R = p->Rp;
     a.x = x;
     a.W = W_base;
     a.y = y;
@@ -375,14 +390,31 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     a.B_slab = p->B_slab;
     a.slots = p->slots_dev;
     a.h = p->h;
-    a.rv = lora::RouteView{p->ro.perm, p->ro.pos_seg, p->ro.segs, p->ro.tiles, p->ro.n_tiles};
+    a.h_parts = 1;
+    a.rv = lora::RouteView{p->ro.perm, p->ro.pos_seg, p->ro.tok_pos, p->ro.tok_seg,
+                           p->ro.segs, p->ro.tiles, p->ro.n_tiles};
     a.tiles_bound = lora::max_tiles(n_tokens, p->S);
     a.policy = p->policy;
-    HIP_TRY(lora::launch_shrink(a, st));
-    HIP_TRY(mark(2));
-    HIP_TRY(lora::launch_base_gemm(a, st));
+    const bool half = p->esz == 2;
+    // Every LoRA bucket is FUSED under the FUSED policy, and under AUTO with
+    // threshold 0 (a bucket holds at least one token): no residual launch then.
+    const bool any_separate = !(p->policy == LORA_MODE_FUSED || (p->policy == LORA_MODE_AUTO && p->theta == 0));
+    if (half && n_tokens <= lora::DECODE_MAX_T) {
+        // Shrink runs inside the decode main kernel.
+        HIP_TRY(mark(2));
+        a.h_parts = lora::decode_h_parts(p->d_in);
+        lora::DecodeArgs d{};
+        d.splits = lora::decode_splits(n_tokens, p->d_in, p->d_out);
+        d.KC = p->d_in / d.splits;
+        d.part = p->gpart;
+        HIP_TRY(lora::launch_gemm_decode(a, d, st));
+    } else {
+        HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
+        HIP_TRY(mark(2));
+        HIP_TRY(lora::launch_base_gemm(a, st));
+    }
     HIP_TRY(mark(3));
-    if (p->policy != LORA_MODE_FUSED) HIP_TRY(lora::launch_expand_separate(a, st));
+    if (any_separate) HIP_TRY(half ? lora::launch_expand_sep16(a, st) : lora::launch_expand_separate(a, st));
     HIP_TRY(mark(4));
     HIP_TRY(record_inflight(p, st));
     return LORA_OK;

@@ -44,6 +44,8 @@ struct RouteOut {
     int32_t *segs;      // [(S+2)*4] {key, start, len, mode}
     int32_t *n_seg;     // [1]
     int32_t *pos_seg;   // [T]   sorted position -> bucket record index
+    int32_t *tok_pos;   // [T]   token -> sorted position (may be null)
+    int32_t *tok_seg;   // [T]   token -> bucket record index (may be null)
     int32_t *tiles;     // [max_tiles*2] {bucket, first row} of LoRA-bucket tiles
     int32_t *n_tiles;   // [1]
     DevStats *stats;    // [1]   may be null
@@ -54,6 +56,8 @@ struct RouteOut {
 struct RouteView {
     const int32_t *perm;
     const int32_t *pos_seg;
+    const int32_t *tok_pos;
+    const int32_t *tok_seg;
     const int32_t *segs;
     const int32_t *tiles;
     const int32_t *n_tiles;
@@ -78,20 +82,36 @@ hipError_t launch_pad_copy(const void *A_user, const void *B_user, void *A_slab,
 
 struct ApplyArgs {
     int dtype;          // lora_dtype
-    int T, d_in, d_out, S, R;
+    int T, d_in, d_out, S;
+    int R;              // slab rank: the pool's max_rank rounded up to a multiple of 8
     const void *x;      // [T][d_in]
     const void *W;      // [d_out][d_in]
     void *y;            // [T][d_out]
     const void *A_slab; // [S][R][d_in]
     const void *B_slab; // [S][d_out][R]
     const SlotDev *slots;
-    float *h;           // [T][R] by sorted position
+    float *h;           // h_parts x [T][R] fp32 by sorted position; h = sum of the parts
+    int h_parts;        // k parts of the shrink, summed in order by the consumers
     RouteView rv;
     int tiles_bound;    // grid bound for tile-parallel kernels
     int policy;         // lora_mode
 };
 
+// Split-K of the decode base GEMM.
+struct DecodeArgs {
+    int splits;         // k chunks per column tile
+    int KC;             // k chunk length (multiple of 32)
+    void *part;         // fp32 partial sums, [splits][d_out/16][TB][64 lanes] fragments
+};
+
 hipError_t launch_shrink(const ApplyArgs &a, hipStream_t st);
+hipError_t launch_shrink16(const ApplyArgs &a, hipStream_t st);
+hipError_t launch_expand_sep16(const ApplyArgs &a, hipStream_t st);
+hipError_t launch_gemm_decode(const ApplyArgs &a, const DecodeArgs &d, hipStream_t st);
+int decode_token_blocks(int T);
+int decode_splits(int T, int d_in, int d_out);
+int decode_h_parts(int d_in);
+constexpr int DECODE_MAX_T = 64;
 hipError_t launch_base_gemm(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_expand_separate(const ApplyArgs &a, hipStream_t st);
 

@@ -154,6 +154,8 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
             if (pos >= 0 && pos < T) {  // always true; keeps a logic error in bounds
                 out.perm[pos] = t;
                 if (out.pos_seg != nullptr) out.pos_seg[pos] = s_seg[key];
+                if (out.tok_pos != nullptr) out.tok_pos[t] = pos;
+                if (out.tok_seg != nullptr) out.tok_seg[t] = s_seg[key];
             }
         }
         __syncthreads();
