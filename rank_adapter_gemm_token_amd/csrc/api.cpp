@@ -411,7 +411,7 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     } else {
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
-        HIP_TRY(lora::launch_base_gemm(a, st));
+        HIP_TRY(half ? lora::launch_gemm_tiled(a, st) : lora::launch_base_gemm(a, st));
     }
     HIP_TRY(mark(3));
     if (any_separate) HIP_TRY(half ? lora::launch_expand_sep16(a, st) : lora::launch_expand_separate(a, st));

@@ -1,5 +1,7 @@
-// apply_kernels.hip -- LoRA shrink, base projection with the fused LoRA expand
-// in its epilogue, and the separate residual expand.
+// apply_kernels.hip -- the fp32 pools' path (VALU, one thread per output):
+// LoRA shrink, base projection with the fused LoRA expand in its epilogue, and
+// the separate residual expand.  fp16/bf16 pools use the MFMA kernels of
+// gemm_decode.hip, gemm_tiled.hip and shrink_expand.hip.
 //
 // "LLM 多 LoRA 推理服务工程 2026", four-layer runtime, execution-unit paragraph:
 // the base linear and the LoRA A/B products either run in one launch (fused)
@@ -62,59 +64,6 @@ __device__ __forceinline__ void finish(const ApplyArgs &a, int row, int col, flo
 
 // ---------------------------------------------------------------- shrink --
 
-// One wave per 16-row tile of one LoRA bucket; MFMA 16x16x32 with the tile's
-// x rows as the A operand and the slot's A rows (rank index j) as the B
-// operand.  RB = ceil(R / 16) blocks of 16 rank columns.
-template <int DT, int RB>
-__global__ __launch_bounds__(64) void k_shrink_mfma(ApplyArgs a) {
-    using E = Elem<DT>;
-    using V = typename E::vec8;
-    const int tile = blockIdx.x;
-    if (tile >= *a.rv.n_tiles) return;
-    const int seg = a.rv.tiles[2 * tile];
-    const int row0 = a.rv.tiles[2 * tile + 1];
-    const int key = a.rv.segs[4 * seg];
-    const int end = a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2];
-    const int rows = min(TILE_ROWS, end - row0);
-
-    const int lane = threadIdx.x & 63;
-    const int r = lane & 15;
-    const int kq = lane >> 4;
-    const bool xv = r < rows;
-    const int t = xv ? token_at(a, row0 + r) : 0;
-    const uint16_t *xp = static_cast<const uint16_t *>(a.x) + static_cast<size_t>(t) * a.d_in + kq * 8;
-    const uint16_t *ap[RB];
-    bool av[RB];
-#pragma unroll
-    for (int cb = 0; cb < RB; ++cb) {
-        const int j = cb * 16 + r;
-        av[cb] = j < a.R;
-        ap[cb] = static_cast<const uint16_t *>(a.A_slab) +
-                 (static_cast<size_t>(key) * a.R + (av[cb] ? j : 0)) * a.d_in + kq * 8;
-    }
-    f32x4_t acc[RB];
-#pragma unroll
-    for (int cb = 0; cb < RB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < a.d_in; k0 += 32) {
-        const V xa = xv ? load8<V>(xp + k0) : zero8<V>();
-#pragma unroll
-        for (int cb = 0; cb < RB; ++cb) {
-            const V b = av[cb] ? load8<V>(ap[cb] + k0) : zero8<V>();
-            acc[cb] = E::mfma(xa, b, acc[cb]);
-        }
-    }
-#pragma unroll
-    for (int cb = 0; cb < RB; ++cb) {
-        const int j = cb * 16 + r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = kq * 4 + i;
-            if (row < rows && j < a.R) a.h[static_cast<size_t>(row0 + row) * a.R + j] = acc[cb][i];
-        }
-    }
-}
-
 // fp32 pools: one thread per (row, rank index) of the tile, sequential k.
 __global__ __launch_bounds__(256) void k_shrink_f32(ApplyArgs a) {
     const int tile = blockIdx.x;
@@ -140,52 +89,6 @@ __global__ __launch_bounds__(256) void k_shrink_f32(ApplyArgs a) {
 }
 
 // ------------------------------------------------------------- base GEMM --
-
-// 64 sorted rows x 64 columns per workgroup of 4 waves; wave w owns columns
-// n0 + 16w .. +15 for all four 16-row blocks.  MFMA 16x16x32: x rows are the
-// A operand, W rows (output columns) the B operand; both are K-contiguous.
-template <int DT>
-__global__ __launch_bounds__(256) void k_gemm_mfma(ApplyArgs a) {
-    using E = Elem<DT>;
-    using V = typename E::vec8;
-    const int n0 = blockIdx.x * 64;
-    const int m0 = blockIdx.y * 64;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int r = lane & 15;
-    const int kq = lane >> 4;
-    const int n = n0 + wave * 16 + r;
-    const uint16_t *wp = static_cast<const uint16_t *>(a.W) + static_cast<size_t>(n) * a.d_in + kq * 8;
-    const uint16_t *xp[4];
-    bool xv[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        const int pos = m0 + rb * 16 + r;
-        xv[rb] = pos < a.T;
-        const int t = xv[rb] ? token_at(a, pos) : 0;
-        xp[rb] = static_cast<const uint16_t *>(a.x) + static_cast<size_t>(t) * a.d_in + kq * 8;
-    }
-    f32x4_t acc[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < a.d_in; k0 += 32) {
-        const V b = load8<V>(wp + k0);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const V xa = xv[rb] ? load8<V>(xp[rb] + k0) : zero8<V>();
-            acc[rb] = E::mfma(xa, b, acc[rb]);
-        }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + rb * 16 + kq * 4 + i;
-            if (row < a.T) finish<DT>(a, row, n, acc[rb][i]);
-        }
-    }
-}
 
 // fp32 pools: one thread per output element, sequential k.
 __global__ __launch_bounds__(256) void k_gemm_f32(ApplyArgs a) {
@@ -231,53 +134,21 @@ __global__ __launch_bounds__(256) void k_expand_separate(ApplyArgs a) {
     }
 }
 
-template <int DT>
-hipError_t shrink_16(const ApplyArgs &a, hipStream_t st) {
-    const dim3 grid(a.tiles_bound);
-    const int rb = (a.R + 15) / 16;
-    switch (rb) {
-        case 1: hipLaunchKernelGGL((k_shrink_mfma<DT, 1>), grid, dim3(64), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((k_shrink_mfma<DT, 2>), grid, dim3(64), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((k_shrink_mfma<DT, 3>), grid, dim3(64), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_shrink_mfma<DT, 4>), grid, dim3(64), 0, st, a); break;
-    }
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_shrink(const ApplyArgs &a, hipStream_t st) {
-    switch (a.dtype) {
-        case DT_F16: return shrink_16<DT_F16>(a, st);
-        case DT_BF16: return shrink_16<DT_BF16>(a, st);
-        default:
-            hipLaunchKernelGGL(k_shrink_f32, dim3(a.tiles_bound), dim3(256), 0, st, a);
-            return hipGetLastError();
-    }
+    hipLaunchKernelGGL(k_shrink_f32, dim3(a.tiles_bound), dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_base_gemm(const ApplyArgs &a, hipStream_t st) {
-    switch (a.dtype) {
-        case DT_F16:
-            hipLaunchKernelGGL(k_gemm_mfma<DT_F16>, dim3(a.d_out / 64, (a.T + 63) / 64), dim3(256), 0, st, a);
-            break;
-        case DT_BF16:
-            hipLaunchKernelGGL(k_gemm_mfma<DT_BF16>, dim3(a.d_out / 64, (a.T + 63) / 64), dim3(256), 0, st, a);
-            break;
-        default:
-            hipLaunchKernelGGL(k_gemm_f32, dim3((a.d_out + 255) / 256, a.T), dim3(256), 0, st, a);
-            break;
-    }
+    hipLaunchKernelGGL(k_gemm_f32, dim3((a.d_out + 255) / 256, a.T), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_expand_separate(const ApplyArgs &a, hipStream_t st) {
     const dim3 grid(a.tiles_bound, (a.d_out + 255) / 256);
-    switch (a.dtype) {
-        case DT_F16: hipLaunchKernelGGL(k_expand_separate<DT_F16>, grid, dim3(256), 0, st, a); break;
-        case DT_BF16: hipLaunchKernelGGL(k_expand_separate<DT_BF16>, grid, dim3(256), 0, st, a); break;
-        default: hipLaunchKernelGGL(k_expand_separate<DT_F32>, grid, dim3(256), 0, st, a); break;
-    }
+    hipLaunchKernelGGL(k_expand_separate<DT_F32>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,151 @@
+// gemm_tiled.hip -- base projection for prefill-shaped calls (T > 64 tokens,
+// fp16/bf16) with the fused LoRA expand in its epilogue.
+//
+// Here the projection is a dense contraction with enough rows to be bound by
+// the matrix cores, not by HBM, so both operands are reused from LDS:
+//   * a workgroup of 4 waves owns a BM x BN output tile (sorted rows x
+//     columns); each wave a (BM/2) x (BN/2) quadrant of 16x16 MFMA blocks;
+//   * K advances in stages of BK = 64: the next stage's x and W fragments are
+//     loaded from global memory into registers while the current stage is
+//     multiplied from LDS, then stored to the other LDS buffer (double
+//     buffering, one barrier per stage);
+//   * LDS holds operands in MFMA fragment order (16 rows x 32 k per 1 KiB
+//     fragment, lane-contiguous), so every operand read is a conflict-free
+//     16-byte LDS read, and every global load moves 16 rows x 64 B;
+//   * x rows are gathered in sorted order (row p = token perm[p]), so the
+//     epilogue adds the LoRA term of FUSED buckets with MFMA over contiguous
+//     buckets, rounds once, and scatters rows back to token order.
+// The tile shape depends on (T, d_out) only.
+#include "epilogue.hpp"
+
+namespace lora {
+
+namespace {
+
+constexpr int BK = 64;  // k per stage: two 32-wide MFMA steps
+
+template <int BM, int BN>
+struct TileShape {
+    static constexpr int TB = BM / 32;          // 16-row blocks per wave
+    static constexpr int WC = BN / 32;          // 16-column blocks per wave
+    static constexpr int FA = BM / 16 * 2;      // A fragments per stage
+    static constexpr int FB = BN / 16 * 2;      // B fragments per stage
+    static constexpr int LA = FA / 4;           // A fragments each wave loads
+    static constexpr int LB = FB / 4;           // B fragments each wave loads
+    static constexpr int STAGE = FA + FB;       // fragments (1 KiB) per stage
+};
+
+template <int DT, int BM, int BN>
+__global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
+    using E = Elem<DT>;
+    using V = typename E::vec8;
+    using Sh = TileShape<BM, BN>;
+    constexpr int TB = Sh::TB;
+    constexpr int WC = Sh::WC;
+    __shared__ u32x4_t lds[2][Sh::STAGE * 64];
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;
+    const int kq = lane >> 4;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int m0 = blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN;
+    const int ksel = wave & 1;  // the k half (of a 64-k stage) this wave loads
+
+    // Fragments this wave loads each stage: A (rb, ksel) for rb = (wave + 4j) / 2,
+    // B (cb, ksel) for cb = (wave + 4j) / 2.  32-bit element offsets from the
+    // (uniform) x and W bases keep the per-lane address state small.
+    const uint16_t *xg = static_cast<const uint16_t *>(a.x) + ksel * 32 + 8 * kq;
+    const uint16_t *wg = static_cast<const uint16_t *>(a.W) + ksel * 32 + 8 * kq;
+    uint32_t xo[Sh::LA];
+    uint32_t xmask = 0;  // bit j: row of A fragment j is a real token
+#pragma unroll
+    for (int j = 0; j < Sh::LA; ++j) {
+        const int p = m0 + ((wave + 4 * j) >> 1) * 16 + r;
+        xmask |= (p < a.T ? 1u : 0u) << j;
+        xo[j] = static_cast<uint32_t>(token_of(a, min(p, a.T - 1))) * static_cast<uint32_t>(a.d_in);
+    }
+    uint32_t wo[Sh::LB];
+#pragma unroll
+    for (int j = 0; j < Sh::LB; ++j)
+        wo[j] = static_cast<uint32_t>(n0 + ((wave + 4 * j) >> 1) * 16 + r) * static_cast<uint32_t>(a.d_in);
+
+    u32x4_t ra[Sh::LA], rbv[Sh::LB];
+    auto load_stage = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < Sh::LA; ++j) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(xg + xo[j] + k0);
+            ra[j] = ((xmask >> j) & 1u) ? v : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::LB; ++j) rbv[j] = *reinterpret_cast<const u32x4_t *>(wg + wo[j] + k0);
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < Sh::LA; ++j) lds[buf][(wave + 4 * j) * 64 + lane] = ra[j];
+#pragma unroll
+        for (int j = 0; j < Sh::LB; ++j) lds[buf][(Sh::FA + wave + 4 * j) * 64 + lane] = rbv[j];
+    };
+
+    f32x4_t acc[TB][WC];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nst = a.d_in / BK;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nst) load_stage((s + 1) * BK);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            // B fragments of the step once; A fragments one row block at a time.
+            V bf[WC];
+#pragma unroll
+            for (int wc = 0; wc < WC; ++wc)
+                bf[wc] = __builtin_bit_cast(V, lds[buf][(Sh::FA + (wn * WC + wc) * 2 + ks) * 64 + lane]);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const V af = __builtin_bit_cast(V, lds[buf][((wm * TB + tb) * 2 + ks) * 64 + lane]);
+#pragma unroll
+                for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(af, bf[wc], acc[tb][wc]);
+            }
+        }
+        if (s + 1 < nst) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    const int pw = m0 + wm * TB * 16;
+    const int nw = n0 + wn * WC * 16;
+    lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, acc);
+    store_rows<DT, TB, WC>(a, pw, a.T, nw, acc);
+}
+
+template <int DT, int BM, int BN>
+hipError_t launch_shape(const ApplyArgs &a, hipStream_t st) {
+    const dim3 grid(a.d_out / BN, (a.T + BM - 1) / BM);
+    hipLaunchKernelGGL((k_gemm_tiled<DT, BM, BN>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const ApplyArgs &a, hipStream_t st) {
+    // Large T: 256 x 256 tiles (high operand reuse).  Otherwise 64-row tiles,
+    // enough of them to fill the chip.
+    if (a.T >= 1024 && a.d_out % 256 == 0) return launch_shape<DT, 256, 256>(a, st);
+    if (a.T >= 512 && a.d_out % 128 == 0) return launch_shape<DT, 128, 128>(a, st);
+    return launch_shape<DT, 64, 64>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tiled(const ApplyArgs &a, hipStream_t st) {
+    return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, st) : launch_dt<DT_BF16>(a, st);
+}
+
+}  // namespace lora

@@ -108,6 +108,7 @@ hipError_t launch_shrink(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_shrink16(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_expand_sep16(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_gemm_decode(const ApplyArgs &a, const DecodeArgs &d, hipStream_t st);
+hipError_t launch_gemm_tiled(const ApplyArgs &a, hipStream_t st);
 int decode_token_blocks(int T);
 int decode_splits(int T, int d_in, int d_out);
 int decode_h_parts(int d_in);
