@@ -33,7 +33,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 ESZ = {"f32": 4, "f16": 2, "bf16": 2}
 TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-KERNEL_SOURCE = os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc", "apply_kernels.hip")
+CSRC = os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc")
+# Dominant kernel of each workload and the sources it is compiled from (their
+# hash keys the committed counter readings to the code they were taken on).
+KERNELS = {
+    "decode": ("k_decode_gemm", ["gemm_decode.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
+    "tiled": ("k_gemm_tiled", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
+}
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -57,12 +63,20 @@ class Call:
         # Whole call: W once, x once, y once, A and B of each distinct adapter
         # touched (true rank) once, plus the index array.
         self.call_bytes = d_in * d_out * e + T * (d_in + d_out) * e + r_sum * (d_in + d_out) * e + 4 * T
-        # Base GEMM kernel (with the fused expand): W, x, y, B of fused buckets.
-        self.gemm_bytes = d_in * d_out * e + T * (d_in + d_out) * e + r_fused * d_out * e
+        # Base GEMM kernel.  Calls of at most 64 tokens (k_decode_gemm, which
+        # also runs the shrink; the split sum, the expand and y belong to its
+        # epilogue kernel): W, x and the true-rank A rows of every adapter
+        # touched.  Larger calls (k_gemm_tiled, whose epilogue adds the fused
+        # expand): W, x, y and the B rows of FUSED buckets.
+        if T <= 64:
+            self.gemm_bytes = d_in * d_out * e + T * d_in * e + r_sum * d_in * e
+        else:
+            self.gemm_bytes = d_in * d_out * e + T * (d_in + d_out) * e + r_fused * d_out * e
         lora_tokens = int(sum(1 for v in idx.cpu().tolist() if v in ranks))
         self.call_flops = 2 * T * d_in * d_out + 2 * sum(
             ranks.get(int(v), 0) for v in idx.cpu().tolist()) * (d_in + d_out)
-        self.gemm_flops = 2 * T * d_in * d_out
+        self.gemm_flops = 2 * T * d_in * d_out + 2 * sum(
+            ranks[int(v)] for v in idx.cpu().tolist() if int(v) in fused_slots) * d_out
         self.lora_tokens = lora_tokens
 
 
@@ -84,19 +98,25 @@ def _buckets(idx_cpu, ranks, policy, theta):
 
 
 def build_linear_copies(L, w, lin, copies, policy, theta):
-    """`copies` independent (pool, W, x, idx, y) sets for one linear."""
+    """`copies` independent (pool, W, x, idx, y) sets for one linear.  theta
+    None keeps the library's default policy."""
     out = []
     ranks = {a.slot: a.rank for a in lin.adapters}
-    distinct, fused = _buckets(w.idx, ranks, policy, theta)
     for c in range(copies):
         pool = L.lora_pool_create(lin.d_in, lin.d_out, w.R, w.S, w.T, TDT[w.dtype])
-        L.lora_set_policy(pool, policy, theta)
+        if theta is not None:
+            L.lora_set_policy(pool, policy, theta)
+        if c == 0:
+            policy, theta = L.lora_get_policy(pool)
+            distinct, fused = _buckets(w.idx, ranks, policy, theta)
         _register(L, pool, lin)
         x = w.x[lin.d_in].cuda().contiguous()
         W = lin.W.cuda().contiguous() if c == 0 else out[0].W.clone()
         idx = w.idx.cuda().contiguous()
         y = torch.empty((w.T, lin.d_out), dtype=TDT[w.dtype], device="cuda")
-        out.append(Call(pool, x, W, idx, y, w.T, lin.d_in, lin.d_out, w.dtype, distinct, ranks, fused))
+        call = Call(pool, x, W, idx, y, w.T, lin.d_in, lin.d_out, w.dtype, distinct, ranks, fused)
+        call.policy, call.theta = policy, theta
+        out.append(call)
     return out
 
 
@@ -170,7 +190,8 @@ def stage_profile(L, steps, K):
     torch.cuda.synchronize()
     run_steps(L, steps, K)
     torch.cuda.synchronize()
-    tot = {"calls": 0, "route_ms": 0.0, "shrink_ms": 0.0, "gemm_ms": 0.0, "expand_ms": 0.0}
+    tot = {"calls": 0, "route_ms": 0.0, "shrink_ms": 0.0, "gemm_ms": 0.0, "expand_ms": 0.0,
+           "kernel_ms": 0.0}
     for p in pools:
         r = L.lora_profile_read(p)
         for k in tot:
@@ -179,21 +200,25 @@ def stage_profile(L, steps, K):
     return tot
 
 
-def kernel_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_hash(kind):
+    h = hashlib.sha256()
+    for name in KERNELS[kind][1]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def traffic_for(workload_key):
-    """HBM bytes per launch from committed rocprofv3 counters, if they were taken
-    on the current kernel source; else None."""
+def traffic_for(workload_key, kind):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter readings, if they were taken on the current kernel sources; else
+    None."""
     try:
         with open(COUNTERS) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     ent = data.get(workload_key)
-    if not ent or ent.get("kernel_sha") != kernel_hash():
+    if not ent or ent.get("kernel_sha") != kernel_hash(kind):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -225,6 +250,37 @@ def cpu_baseline(w, seconds):
 
 # ----------------------------------------------------------------------------
 
+def theta_sweep(L, args):
+    """The fused/separate sweep on the 100-adapter workload: tokens/s of every
+    policy at T in {1, 8, 16, 32, 64}; the threshold whose geometric mean over
+    T is highest is the device's threshold.  Prints one JSON line."""
+    from rank_adapter_gemm_token_amd import workloads as wl
+    policies = [("separate", 2, 16), ("fused", 1, 16)] + [("auto%d" % t, 0, t) for t in (0, 1, 2, 4, 8, 16, 32, 64)]
+    table = {}
+    for T in wl.SWEEP_T:
+        w = wl.sweep(T)
+        calls = build_linear_copies(L, w, w.linears[0], args.copies, 0, 16)
+        steps = [[c] for c in calls]
+        row = {}
+        for name, pol, th in policies:
+            for c in calls:
+                L.lora_set_policy(c.pool, pol, th)
+            run_steps(L, steps, args.warmup)
+            torch.cuda.synchronize()
+            sec = timed(L, steps, args.steps)
+            row[name] = T * args.steps / sec
+        table[T] = row
+        log("T=%d" % T, {k: round(v) for k, v in row.items()})
+        for c in calls:
+            L.lora_pool_destroy(c.pool)
+    gm = {name: float(np.exp(np.mean([np.log(table[T][name]) for T in table]))) for name, _, _ in policies}
+    best = max((n for n in gm if n.startswith("auto")), key=lambda n: gm[n])
+    print(json.dumps({"sweep": "fused/separate threshold, 4096x4096 fp16, 100 adapters r8, Zipf(1.1)",
+                      "unit": "tokens/s", "steps": args.steps, "copies": args.copies,
+                      "per_T": {str(T): table[T] for T in table}, "geomean": gm,
+                      "best_auto": best, "theta_star": int(best[4:])}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,11 +290,16 @@ def main():
                     help="decode (default) | sweep<T> | prefill | stack")
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--policy", type=int, default=0, help="0 auto, 1 fused, 2 separate")
-    ap.add_argument("--theta", type=int, default=None)
+    ap.add_argument("--policy", type=int, default=0, help="0 auto, 1 fused, 2 separate (with --theta)")
+    ap.add_argument("--theta", type=int, default=None, help="threshold; default: the library's policy")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-stage pass")
+    ap.add_argument("--theta-sweep", action="store_true",
+                    help="run the fused/separate threshold sweep instead of the bench step")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before warm-up, run two plain device-to-device copies of this many MiB "
+                         "(the known-size reference for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -250,10 +311,19 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     from rank_adapter_gemm_token_amd import lora as L
-    if args.theta is None:
-        args.theta = 16
+    if args.theta_sweep:
+        theta_sweep(L, args)
+        return
 
     w, steps, desc = setup(args, L)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log("workload:", desc, "| step sets:", len(steps), "| calls/step:", len(steps[0]))
     run_steps(L, steps, args.warmup)
     torch.cuda.synchronize()
@@ -273,9 +343,12 @@ def main():
         prof = stage_profile(L, steps, args.steps)
         n = prof["calls"]
         stages = {k: prof[k] / n for k in ("route_ms", "shrink_ms", "gemm_ms", "expand_ms")}
+        kernel_s = prof["kernel_ms"] / n / 1e3
         log("per-call stage ms (events):", {k: round(v * 1e3, 2) for k, v in stages.items()}, "us")
         calls_per_step = len(calls)
-        gemm_s = stages["gemm_ms"] / 1e3
+        # The dominant kernel's own device time (dispatch timestamps recorded
+        # by its launch), averaged over the K calls of the profile pass.
+        gemm_s = kernel_s
         if mfma_bound:
             achieved = (sum(c.gemm_flops for c in calls) / calls_per_step) / gemm_s / 1e12
             roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[w.dtype],
@@ -285,8 +358,10 @@ def main():
             achieved = per_launch / gemm_s / 1e9
             roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS}
-        roof["kernel"] = "k_gemm_mfma (base GEMM + fused expand)"
-        roof["traffic"] = traffic_for(args.workload)
+        kind = "decode" if calls[0].T <= 64 else "tiled"
+        roof["kernel"] = KERNELS[kind][0]
+        roof["kernel_us"] = gemm_s * 1e6
+        roof["traffic"] = traffic_for(args.workload, kind)
 
     cpu = None
     if not args.no_cpu_baseline and (args.workload == "decode" or args.workload.startswith("sweep")):
@@ -310,7 +385,7 @@ def main():
                 "N(0,0.01) B)",
         "config": {"workload": desc, "tokens_per_step": tokens_per_step,
                    "calls_per_step": len(calls), "weight_copies": len(steps),
-                   "policy": ["auto", "fused", "separate"][args.policy], "theta": args.theta,
+                   "policy": ["auto", "fused", "separate"][calls[0].policy], "theta": calls[0].theta,
                    "step_bytes_alg": step_bytes, "step_flops_alg": step_flops},
         "step_roofline": {"hbm_GBs": step_bytes / step_s / 1e9,
                           "hbm_frac": step_bytes / step_s / 1e9 / HBM_PEAK_GBS,

@@ -226,14 +226,21 @@ int lora_poll_errors(lora_pool p, uint64_t *n_invalid_tokens);
  * lora_apply (up to max_calls of them between two reads) records HIP timing
  * events on its own stream before routing and after the routing, shrink,
  * base-GEMM and separate-expand launches; a stage's time is the interval
- * between its two events.  Events are created by lora_profile_enable, not on
- * the hot path.  enable = 0 turns it off and frees the events. */
+ * between its two events.  The base-GEMM kernel is also launched with a pair
+ * of events that its dispatch records itself (kernel_ms: the kernel's own
+ * device time, no launch gaps).  Events are created by lora_profile_enable,
+ * not on the hot path.  enable = 0 turns it off and frees the events. */
 typedef struct {
     int64_t calls;      /* timed lora_apply calls since the last read */
     double route_ms;    /* summed over those calls */
     double shrink_ms;
-    double gemm_ms;     /* base projection, including the fused expand */
+    double gemm_ms;     /* base projection with the fused expand.  fp16/bf16
+                           calls of at most 64 tokens route and shrink inside
+                           the base-GEMM launch: route_ms and shrink_ms are 0
+                           and gemm_ms also holds its split-sum epilogue */
     double expand_ms;   /* separate residual expand */
+    double kernel_ms;   /* device time of the base-GEMM kernel itself (fp16/
+                           bf16 pools; 0 for fp32) */
 } lora_profile;
 
 int lora_profile_enable(lora_pool p, int enable, int max_calls);

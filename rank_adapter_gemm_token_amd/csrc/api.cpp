@@ -6,6 +6,7 @@
 // every buffer lora_apply touches is carved out of the pool at creation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -57,9 +58,14 @@ private:
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Default fused/separate threshold.  The pages give 16 for other GPUs and ask
-// for a per-GPU value; this is the gfx950 value the library ships.
-constexpr int kDefaultTheta = 16;
+// Default fused/separate threshold of gfx950.  The threshold is tuned per GPU
+// model ("LLM 多 LoRA 推理服务工程 2026", SRE list item 11; the routing-layer
+// paragraph gives 16 for other GPUs).  On MI355X the sweep over the
+// 100-adapter workload at T = 1 .. 64 puts every AUTO threshold above 0
+// about 20% below all-fused: the fused expand adds little to the base GEMM's
+// epilogue, a separate bucket costs one more launch and a y round trip.  So:
+// every LoRA bucket fused.
+constexpr int kDefaultTheta = 0;
 
 }  // namespace
 
@@ -79,7 +85,7 @@ struct lora_pool_s {
 
     lora::RouteOut ro{};
     float *h = nullptr;
-    void *gpart = nullptr;
+    float *part = nullptr;  // decode split-K partial sums
 
     hipStream_t internal = nullptr;
     std::mutex mu;
@@ -89,7 +95,7 @@ struct lora_pool_s {
 
     // Opt-in stage timing (lora_profile_enable).
     struct ProfSet {
-        hipEvent_t e[5];
+        hipEvent_t e[7];  // stage marks 0..4; 5, 6: the base-GEMM kernel's own start / stop
     };
     std::vector<ProfSet> prof;
     size_t prof_used = 0;
@@ -230,12 +236,13 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     const size_t o_ntiles = take(4);
     const size_t o_stats = take(sizeof(lora::DevStats));
     const size_t o_err = take(8);
-    // h: up to 8 k parts of [T][Rp] fp32 (the decode shrink's parts).
-    const size_t o_h = take(8 * T * Rp * 4);
-    // Split-K partial sums of the decode GEMM: splits x d_out x T_pad fp32.
-    const size_t o_gpart = take(esz == 2 ? static_cast<size_t>(lora::decode_splits(static_cast<int>(dec_T), d_in, d_out)) *
-                                               16 * lora::decode_token_blocks(static_cast<int>(dec_T)) * d_out * 4
-                                         : 0);
+    // h: fp32 by sorted row, [T][Rp]; calls of at most 64 tokens (fp16/bf16)
+    // keep one part per k split of their GEMM, [splits][T][Rp], and the
+    // splits' partial sums [splits][T][d_out].
+    const int dec_splits = (esz == 2) ? lora::decode_splits(static_cast<int>(dec_T), d_in) : 0;
+    const size_t h_rows = std::max(T, static_cast<size_t>(dec_splits) * dec_T);
+    const size_t o_h = take(h_rows * Rp * 4);
+    const size_t o_part = take(static_cast<size_t>(dec_splits) * dec_T * d_out * 4);
     const size_t ws_bytes = off;
 
     e = hipMalloc(&p->A_slab, a_bytes);
@@ -268,7 +275,7 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     p->ro.stats = reinterpret_cast<lora::DevStats *>(w + o_stats);
     p->ro.err = reinterpret_cast<unsigned long long *>(w + o_err);
     p->h = reinterpret_cast<float *>(w + o_h);
-    p->gpart = w + o_gpart;
+    p->part = reinterpret_cast<float *>(w + o_part);
     *out = p;
     return LORA_OK;
 }
@@ -371,11 +378,9 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     hipStream_t st = static_cast<hipStream_t>(stream);
     lora_pool_s::ProfSet *ps = (p->prof_used < p->prof.size()) ? &p->prof[p->prof_used++] : nullptr;
     auto mark = [&](int i) { return ps ? hipEventRecord(ps->e[i], st) : hipSuccess; };
+    lora::LaunchEvents kev{};
+    if (ps) kev = lora::LaunchEvents{ps->e[5], ps->e[6]};
 
-    HIP_TRY(mark(0));
-    HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
-                               p->ro, st));
-    HIP_TRY(mark(1));
     lora::ApplyArgs a{};
     a.dtype = p->dtype;
     a.T = n_tokens;
@@ -399,19 +404,36 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     // Every LoRA bucket is FUSED under the FUSED policy, and under AUTO with
     // threshold 0 (a bucket holds at least one token): no residual launch then.
     const bool any_separate = !(p->policy == LORA_MODE_FUSED || (p->policy == LORA_MODE_AUTO && p->theta == 0));
-    if (half && n_tokens <= lora::DECODE_MAX_T) {
-        // Shrink runs inside the decode main kernel.
-        HIP_TRY(mark(2));
-        a.h_parts = lora::decode_h_parts(p->d_in);
+
+    HIP_TRY(mark(0));
+    const int dsplits = (half && n_tokens <= lora::DECODE_MAX_T) ? lora::decode_splits(n_tokens, p->d_in) : 0;
+    if (dsplits > 0) {
+        // Routing, shrink and the split-K GEMM in one launch, then the
+        // epilogue (split sum, fused expand, rounding).
         lora::DecodeArgs d{};
-        d.splits = lora::decode_splits(n_tokens, p->d_in, p->d_out);
-        d.KC = p->d_in / d.splits;
-        d.part = p->gpart;
-        HIP_TRY(lora::launch_gemm_decode(a, d, st));
+        d.splits = dsplits;
+        d.route_groups = std::max(1, std::min(std::min(n_tokens, p->S), p->d_out / 64));
+        d.max_rank = p->R;
+        d.theta = p->theta;
+        d.part = p->part;
+        a.h_parts = dsplits;
+        HIP_TRY(mark(1));
+        HIP_TRY(mark(2));
+        HIP_TRY(lora::launch_decode_gemm(a, d, token_adapter_idx, p->ro, st, kev));
+        HIP_TRY(lora::launch_decode_epilogue(a, d, st));
     } else {
+        HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
+                                   p->ro, st));
+        HIP_TRY(mark(1));
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
-        HIP_TRY(half ? lora::launch_gemm_tiled(a, st) : lora::launch_base_gemm(a, st));
+        if (half) {
+            HIP_TRY(lora::launch_gemm_tiled(a, st, kev));
+        } else {
+            HIP_TRY(lora::launch_base_gemm(a, st));
+            HIP_TRY(mark(5));
+            HIP_TRY(mark(6));
+        }
     }
     HIP_TRY(mark(3));
     if (any_separate) HIP_TRY(half ? lora::launch_expand_sep16(a, st) : lora::launch_expand_separate(a, st));
@@ -541,6 +563,9 @@ int lora_profile_read(lora_pool p, lora_profile *out) {
             HIP_TRY(hipEventElapsedTime(&ms, ps.e[i], ps.e[i + 1]));
             *acc[i] += ms;
         }
+        float ms = 0.0f;
+        HIP_TRY(hipEventElapsedTime(&ms, ps.e[5], ps.e[6]));
+        out->kernel_ms += ms;
     }
     out->calls = static_cast<int64_t>(p->prof_used);
     p->prof_used = 0;

@@ -62,10 +62,31 @@ struct Elem<DT_BF16> {
     }
 };
 
+// A value every lane of the wave holds, moved to a scalar register so that
+// the compiler sees it as uniform: branches on it become scalar branches.
+// Control flow around MFMA must be uniform in that sense -- MFMA does not
+// honour EXEC, so an MFMA in a lane-masked block still executes.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // 16-byte load of eight 16-bit elements as an MFMA operand.
 template <typename V>
 __device__ __forceinline__ V load8(const uint16_t *p) {
     return __builtin_bit_cast(V, *reinterpret_cast<const u32x4_t *>(p));
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9 family descriptor,
+// word 3 = 0x00020000).  Loads through it address base + soffset + voffset +
+// immediate; voffset + immediate at or past `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                             0x00020000);
+}
+
+// 16-byte buffer load as an MFMA operand (byte offsets).
+template <typename V>
+__device__ __forceinline__ V bload8(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff),
+                                                                        static_cast<int>(soff), 0));
 }
 
 template <typename V>

@@ -29,22 +29,23 @@ __device__ __forceinline__ int token_of(const ApplyArgs &a, int p) {
 }
 
 // Partial h = x_tile . A_slot^T over k part `part` (of h_parts) for one
-// 16-row tile of an adapter bucket.  One workgroup of NWV waves; the part's k
-// steps are split over the waves and the waves' sums are added in LDS in a
-// fixed order.  `lds` holds >= NWV * RB * 64 16-byte words.  The part is
-// written to h + part * T * R; consumers add the parts in order.
+// 16-row tile of an adapter bucket: slot `key`, sorted rows row0 .. row0 +
+// rows - 1, whose tokens are perm[row0 ..] (perm may live in LDS or global
+// memory).  One workgroup of NWV waves; the part's k steps are split over the
+// waves and the waves' sums are added in LDS in a fixed order.  `lds` holds
+// >= NWV * RB * 64 16-byte words.  The part is written to h + part * T * R;
+// consumers add the parts in order.
 template <int DT, int RB, int NWV>
-__device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int part, u32x4_t *lds) {
+__device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row0, int rows, const int32_t *perm,
+                                            int part, u32x4_t *lds) {
     using E = Elem<DT>;
     using V = typename E::vec8;
-    if (tile >= *a.rv.n_tiles) return;
-    const int seg = a.rv.tiles[2 * tile];
-    const int row0 = a.rv.tiles[2 * tile + 1];
-    const int key = a.rv.segs[4 * seg];
-    const int end = a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2];
-    const int rows = min(TILE_ROWS, end - row0);
+    key = uniform(key);
+    row0 = uniform(row0);
+    rows = uniform(rows);
+    part = uniform(part);
     const int Rp = a.R;
-    const int wave = threadIdx.x >> 6;
+    const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int kq = lane >> 4;
@@ -55,8 +56,8 @@ __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int pa
     const int ke = (split + 1) * kst / nsplit;
 
     const bool xv = r < rows;
-    const uint16_t *xp = static_cast<const uint16_t *>(a.x) +
-                         static_cast<size_t>(token_of(a, min(row0 + r, end - 1))) * a.d_in + 8 * kq;
+    const int tok = min(max(perm[row0 + min(r, rows - 1)], 0), a.T - 1);
+    const uint16_t *xp = static_cast<const uint16_t *>(a.x) + static_cast<size_t>(tok) * a.d_in + 8 * kq;
     const uint16_t *ap[RB];
     bool av[RB];
 #pragma unroll
@@ -70,7 +71,7 @@ __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int pa
 #pragma unroll
     for (int cb = 0; cb < RB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int U = RB <= 2 ? 8 : 4;  // k steps whose loads are all in flight together
+    constexpr int U = RB == 1 ? 16 : RB == 2 ? 8 : 4;  // k steps whose loads are all in flight together
     for (int k0 = kb; k0 < ke; k0 += U) {
         V xa[U];
         V b[U][RB];
@@ -108,6 +109,17 @@ __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int pa
     }
 }
 
+// shrink_unit for tile `tile` of the routing in global memory.
+template <int DT, int RB, int NWV>
+__device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int part, u32x4_t *lds) {
+    if (tile >= uniform(*a.rv.n_tiles)) return;
+    const int seg = a.rv.tiles[2 * tile];
+    const int row0 = a.rv.tiles[2 * tile + 1];
+    const int key = a.rv.segs[4 * seg];
+    const int end = a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2];
+    shrink_unit<DT, RB, NWV>(a, key, row0, min(TILE_ROWS, end - row0), a.rv.perm, part, lds);
+}
+
 // h[p][j .. j+7] summed over the shrink's k parts in order.
 __device__ __forceinline__ void load_h8(const ApplyArgs &a, int p, int j, float (&hv)[8]) {
     const size_t stride = static_cast<size_t>(a.T) * a.R;
@@ -137,17 +149,20 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
     const int r = lane & 15;
     const int kq = lane >> 4;
     const int Rp = a.R;
+    p0 = uniform(p0);
+    rows_end = uniform(rows_end);
+    n0 = uniform(n0);
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const int pb = p0 + tb * 16;
         if (pb >= rows_end) break;
-        const int g0 = a.rv.pos_seg[pb];
-        const int g1 = a.rv.pos_seg[min(pb + 15, rows_end - 1)];
+        const int g0 = uniform(a.rv.pos_seg[pb]);
+        const int g1 = uniform(a.rv.pos_seg[min(pb + 15, rows_end - 1)]);
         const int ph = pb + r;  // this lane's row in the H operand
         const int gh = (ph < rows_end) ? a.rv.pos_seg[ph] : -1;
         for (int g = g0; g <= g1; ++g) {
-            const int key = a.rv.segs[4 * g];
-            const int mode = a.rv.segs[4 * g + 3];
+            const int key = uniform(a.rv.segs[4 * g]);
+            const int mode = uniform(a.rv.segs[4 * g + 3]);
             if (key >= a.S || mode != want) continue;
             const float s = a.slots[key].scale;
             for (int js = 0; js < Rp; js += 32) {

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
     constexpr int WC = Sh::WC;
     __shared__ u32x4_t lds[2][Sh::STAGE * 64];
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int kq = lane >> 4;
@@ -127,25 +127,25 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
 }
 
 template <int DT, int BM, int BN>
-hipError_t launch_shape(const ApplyArgs &a, hipStream_t st) {
+hipError_t launch_shape(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
     const dim3 grid(a.d_out / BN, (a.T + BM - 1) / BM);
-    hipLaunchKernelGGL((k_gemm_tiled<DT, BM, BN>), grid, dim3(256), 0, st, a);
+    LORA_LAUNCH(ev, (k_gemm_tiled<DT, BM, BN>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_dt(const ApplyArgs &a, hipStream_t st) {
-    // Large T: 256 x 256 tiles (high operand reuse).  Otherwise 64-row tiles,
-    // enough of them to fill the chip.
-    if (a.T >= 1024 && a.d_out % 256 == 0) return launch_shape<DT, 256, 256>(a, st);
-    if (a.T >= 512 && a.d_out % 128 == 0) return launch_shape<DT, 128, 128>(a, st);
-    return launch_shape<DT, 64, 64>(a, st);
+hipError_t launch_dt(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
+    // Large T: 128 x 128 tiles (two workgroups per CU by LDS; a 256 x 256
+    // tile needs more than the 256 registers a lane has at that occupancy).
+    // Otherwise 64 x 64 tiles, enough of them to fill the chip.
+    if (a.T >= 512 && a.d_out % 128 == 0) return launch_shape<DT, 128, 128>(a, st, ev);
+    return launch_shape<DT, 64, 64>(a, st, ev);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_tiled(const ApplyArgs &a, hipStream_t st) {
-    return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, st) : launch_dt<DT_BF16>(a, st);
+hipError_t launch_gemm_tiled(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
+    return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, st, ev) : launch_dt<DT_BF16>(a, st, ev);
 }
 
 }  // namespace lora

@@ -2,6 +2,7 @@
 // and the .hip kernel files of liblora.so.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -97,22 +98,46 @@ struct ApplyArgs {
     int policy;         // lora_mode
 };
 
-// Split-K of the decode base GEMM.
-struct DecodeArgs {
-    int splits;         // k chunks per column tile
-    int KC;             // k chunk length (multiple of 32)
-    void *part;         // fp32 partial sums, [splits][d_out/16][TB][64 lanes] fragments
-};
-
 hipError_t launch_shrink(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_shrink16(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_expand_sep16(const ApplyArgs &a, hipStream_t st);
-hipError_t launch_gemm_decode(const ApplyArgs &a, const DecodeArgs &d, hipStream_t st);
-hipError_t launch_gemm_tiled(const ApplyArgs &a, hipStream_t st);
-int decode_token_blocks(int T);
-int decode_splits(int T, int d_in, int d_out);
-int decode_h_parts(int d_in);
+// Optional timing events of one launch: when `start` is set, the kernel is
+// launched with hipExtLaunchKernelGGL, which records both events from the
+// dispatch itself (the kernel's own device time, no inter-launch gap).
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+#define LORA_LAUNCH(ev, kernel, grid, block, shmem, st, ...)                                             \
+    do {                                                                                                \
+        if ((ev).start)                                                                                 \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, (ev).start, (ev).stop, 0u, __VA_ARGS__); \
+        else                                                                                            \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);                            \
+    } while (0)
+
+// Calls of at most DECODE_MAX_T tokens (fp16/bf16): routing, shrink and the
+// split-K base GEMM in one launch (writes `out`, h parts and the partial
+// sums), then the epilogue (split sum, fused expand, rounding, store).
 constexpr int DECODE_MAX_T = 64;
+constexpr int MAX_DSPLIT = 16;
+struct DecodeArgs {
+    int splits;         // k splits = h parts (decode_splits)
+    int route_groups;   // column groups whose workgroups route (and shrink)
+    int max_rank;       // the pool's rank, for the padded-row statistic
+    int theta;          // fused threshold
+    float *part;        // fp32 partial sums [splits][T][d_out]
+};
+hipError_t launch_decode_gemm(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
+                              hipStream_t st, LaunchEvents ev = {});
+hipError_t launch_decode_epilogue(const ApplyArgs &a, const DecodeArgs &d, hipStream_t st);
+// k splits of the decode GEMM for (T, d_in); 0 if d_in is too large for it.
+int decode_splits(int T, int d_in);
+int decode_token_blocks(int T);
+// Larger calls (fp16/bf16): LDS-tiled MFMA GEMM with the fused expand.
+hipError_t launch_gemm_tiled(const ApplyArgs &a, hipStream_t st, LaunchEvents ev = {});
+// fp32 pools: VALU base GEMM and residual expand.
 hipError_t launch_base_gemm(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_expand_separate(const ApplyArgs &a, hipStream_t st);
 

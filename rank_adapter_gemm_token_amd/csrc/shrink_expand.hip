@@ -32,13 +32,13 @@ __global__ __launch_bounds__(256) void k_expand_sep(ApplyArgs a) {
     using E = Elem<DT>;
     using raw = typename E::raw;
     const int tile = blockIdx.x;
-    if (tile >= *a.rv.n_tiles) return;
-    const int seg = a.rv.tiles[2 * tile];
-    if (a.rv.segs[4 * seg + 3] != SEG_SEPARATE) return;
-    const int row0 = a.rv.tiles[2 * tile + 1];
-    const int end = a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2];
+    if (tile >= uniform(*a.rv.n_tiles)) return;
+    const int seg = uniform(a.rv.tiles[2 * tile]);
+    if (uniform(a.rv.segs[4 * seg + 3]) != SEG_SEPARATE) return;
+    const int row0 = uniform(a.rv.tiles[2 * tile + 1]);
+    const int end = uniform(a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2]);
     const int rows_end = min(row0 + TILE_ROWS, end);
-    const int wave = threadIdx.x >> 6;
+    const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int kq = lane >> 4;

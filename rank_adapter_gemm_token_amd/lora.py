@@ -61,7 +61,8 @@ class lora_stats(ctypes.Structure):
 
 class lora_profile(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64), ("route_ms", ctypes.c_double), ("shrink_ms", ctypes.c_double),
-                ("gemm_ms", ctypes.c_double), ("expand_ms", ctypes.c_double)]
+                ("gemm_ms", ctypes.c_double), ("expand_ms", ctypes.c_double),
+                ("kernel_ms", ctypes.c_double)]
 
 
 _vp = ctypes.c_void_p

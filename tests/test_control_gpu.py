@@ -219,3 +219,42 @@ def test_stats_zero_pad_fraction():
         assert p.poll_errors() == 1
     finally:
         p.close()
+
+
+def test_stage_profile_counts_calls_and_stages():
+    # Opt-in stage timing: one event set per call, every stage non-negative.
+    d = 1024
+    p = Pool(d, d, 16, 2, 128, "f16")
+    try:
+        A, B = _adapter(d, d, 16)
+        p.register(0, A, B, 16, 32.0)
+        W = dev(torch.randn(d, d).to(torch.float16) / 32)
+        lora.lora_profile_enable(p.h, 1, 8)
+        for T in (64, 64, 64):
+            p.apply(dev(torch.randn(T, d).to(torch.float16)), W, dev(torch.zeros(T, dtype=torch.int32)))
+        r = lora.lora_profile_read(p.h)
+        assert r["calls"] == 3
+        assert r["gemm_ms"] > 0 and r["route_ms"] < r["gemm_ms"] and r["shrink_ms"] < r["gemm_ms"]
+        # The main kernel's own dispatch time lies inside its stage interval.
+        assert 0 < r["kernel_ms"] <= r["gemm_ms"] + 1e-3
+        assert min(r[k] for k in r if k.endswith("_ms")) >= 0
+        for T in (128, 128):
+            p.apply(dev(torch.randn(T, d).to(torch.float16)), W, dev(torch.zeros(T, dtype=torch.int32)))
+        r = lora.lora_profile_read(p.h)
+        assert r["calls"] == 2 and r["gemm_ms"] > 0 and r["shrink_ms"] > 0 and r["route_ms"] > 0
+        assert 0 < r["kernel_ms"] <= r["gemm_ms"] + 1e-3
+        lora.lora_profile_enable(p.h, 0)
+        p.apply(dev(torch.randn(8, d).to(torch.float16)), W, dev(torch.zeros(8, dtype=torch.int32)))
+        assert lora.lora_profile_read(p.h)["calls"] == 0
+    finally:
+        p.close()
+
+
+def test_default_policy_is_the_gfx950_threshold():
+    # AUTO with the threshold the library ships for gfx950 (every LoRA bucket
+    # fused, from the fused/separate sweep).
+    p = Pool(64, 64, 8, 2, 4, "f16")
+    try:
+        assert lora.lora_get_policy(p.h) == (lora.LORA_MODE_AUTO, 0)
+    finally:
+        p.close()
