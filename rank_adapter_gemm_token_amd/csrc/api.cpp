@@ -236,13 +236,14 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     const size_t o_ntiles = take(4);
     const size_t o_stats = take(sizeof(lora::DevStats));
     const size_t o_err = take(8);
-    // h: fp32 by sorted row, [T][Rp]; calls of at most 64 tokens (fp16/bf16)
-    // keep one part per k split of their GEMM, [splits][T][Rp], and the
-    // splits' partial sums [splits][T][d_out].
+    // h: fp32, [T][Rp]; calls of at most 64 tokens (fp16/bf16) keep one part
+    // per k split of their GEMM, [splits][T][Rp], and the splits' partial
+    // sums [splits][T rounded up to 16 .. 64][d_out].
     const int dec_splits = (esz == 2) ? lora::decode_splits(static_cast<int>(dec_T), d_in) : 0;
     const size_t h_rows = std::max(T, static_cast<size_t>(dec_splits) * dec_T);
     const size_t o_h = take(h_rows * Rp * 4);
-    const size_t o_part = take(static_cast<size_t>(dec_splits) * dec_T * d_out * 4);
+    const size_t dec_rows = static_cast<size_t>(lora::decode_token_blocks(static_cast<int>(dec_T))) * 16;
+    const size_t o_part = take(static_cast<size_t>(dec_splits) * dec_rows * d_out * 4);
     const size_t ws_bytes = off;
 
     e = hipMalloc(&p->A_slab, a_bytes);
@@ -408,19 +409,18 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     HIP_TRY(mark(0));
     const int dsplits = (half && n_tokens <= lora::DECODE_MAX_T) ? lora::decode_splits(n_tokens, p->d_in) : 0;
     if (dsplits > 0) {
-        // Routing, shrink and the split-K GEMM in one launch, then the
-        // epilogue (split sum, fused expand, rounding).
+        // Split-K GEMM with the shrink, then the epilogue, which routes,
+        // sums the splits and adds the fused expand.
         lora::DecodeArgs d{};
         d.splits = dsplits;
-        d.route_groups = std::max(1, std::min(std::min(n_tokens, p->S), p->d_out / 64));
         d.max_rank = p->R;
         d.theta = p->theta;
         d.part = p->part;
         a.h_parts = dsplits;
+        a.h_by_token = 1;
         HIP_TRY(mark(1));
         HIP_TRY(mark(2));
-        HIP_TRY(lora::launch_decode_gemm(a, d, token_adapter_idx, p->ro, st, kev));
-        HIP_TRY(lora::launch_decode_epilogue(a, d, st));
+        HIP_TRY(lora::launch_decode(a, d, token_adapter_idx, p->ro, st, kev));
     } else {
         HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
                                    p->ro, st));

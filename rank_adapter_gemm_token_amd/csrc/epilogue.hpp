@@ -120,7 +120,8 @@ __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int pa
     shrink_unit<DT, RB, NWV>(a, key, row0, min(TILE_ROWS, end - row0), a.rv.perm, part, lds);
 }
 
-// h[p][j .. j+7] summed over the shrink's k parts in order.
+// h[p][j .. j+7] summed over the shrink's k parts in order (p: the h row,
+// a sorted position or a token).
 __device__ __forceinline__ void load_h8(const ApplyArgs &a, int p, int j, float (&hv)[8]) {
     const size_t stride = static_cast<size_t>(a.T) * a.R;
     const float4 *hp = reinterpret_cast<const float4 *>(a.h + static_cast<size_t>(p) * a.R + j);
@@ -171,7 +172,7 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
                 V hf = zero8<V>();
                 if (jv && gh == g) {
                     float hv[8];
-                    load_h8(a, ph, j, hv);
+                    load_h8(a, a.h_by_token ? token_of(a, ph) : ph, j, hv);
                     typename E::raw hr[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) hr[e] = E::from_f(s * hv[e]);

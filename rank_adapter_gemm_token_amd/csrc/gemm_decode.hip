@@ -1,5 +1,5 @@
 // gemm_decode.hip -- the decode path (T <= 64 tokens per call, fp16/bf16):
-// routing, LoRA shrink, base projection and the fused LoRA expand in two
+// base projection, LoRA shrink, routing and the fused LoRA expand in two
 // launches.
 //
 // At decode sizes a call is bound by streaming W (d_out x d_in, read once)
@@ -7,35 +7,35 @@
 // layout in which each CU covers a few columns over the whole of d_in reads
 // x from L2 once per CU (128 MiB at d_in = 4096, T = 64, 256 CUs).  Here a
 // workgroup covers 64 columns over one k split of d_in (x traffic / 4), and
-// the splits' fp32 partial sums are added by a second, small kernel that
-// also applies the LoRA term:
+// the splits' fp32 partial sums are added by a second, small kernel, which
+// also routes the tokens and applies the LoRA term.  Nothing in the first
+// kernel waits for routing:
 //
-// k_decode_gemm -- workgroup (column group of 64, k split q), 4 waves (one
-//   per SIMD, 512 registers each); wave w holds the split's k steps w, w+4,
-//   ..., w+28 for all 64 columns and all T rows.
-//   * Loads are issued in the order they are needed and all at once, through
-//     buffer resources (uniform column-block and step offsets): the adapter
-//     indices and the slot table (routing workgroups), then every x and W
-//     fragment of the wave -- the whole of the workgroup's W tile is in
-//     flight from the start.
-//   * Routing workgroups sort the (at most 64) tokens by adapter in LDS, in
-//     one wave: each token's sorted position by comparing keys, then
-//     buckets, modes and tiles from ballots -- the same stable order as the
-//     routing kernel of larger calls.  Workgroup 0 publishes it (permutation,
-//     bucket records, tiles, statistics, invalid-token count).  The A rows of
-//     the workgroup's first LoRA bucket are requested right after.
+// k_decode_gemm -- workgroup (column group c of 64 columns, k split q), 4
+//   waves (one per SIMD, 512 registers each); wave w holds the split's k
+//   steps w, w+4, ..., w+28 for all 64 columns and all T rows.
+//   * Loads are issued all at once, through buffer resources (uniform
+//     column-block and step offsets): the adapter index of every token, the
+//     A rows of slot c for the split's steps (requested before the token
+//     indices are known -- they are few), then every x and W fragment of the
+//     wave, so the whole of the workgroup's W tile is in flight from the
+//     start.
 //   * GEMM: fp32 MFMA accumulators over the wave's steps; the 4 waves' sums
-//     are added in LDS in a fixed order and the split's partial sums stored,
-//     coalesced.
-//   * Shrink: the workgroups of column group c also compute, for LoRA
-//     buckets c, c + groups, ..., this split's part of h = x . A_slot^T for
-//     all T rows from the x fragments they hold, keeping the bucket's rows
-//     (fp32, by sorted row, part q).
-// k_decode_epilogue -- 16 columns per workgroup, rows in token order: adds
-//   the splits' partial sums in a fixed order, adds s * h . B for FUSED
-//   buckets (h = the parts summed in order, fp32 VALU), rounds once and
-//   stores; invalid tokens get NaN.  SEPARATE rows keep the rounded base for
-//   the residual kernel.
+//     are added in LDS in a fixed order and stored as the split's partial
+//     sums in MFMA fragment order (16 bytes a lane, coalesced).
+//   * Shrink: for slots c, c + groups, ... that some token names and that
+//     are active, this split's part of h = x . A_slot^T for all T rows from
+//     the x fragments already held, rows of that slot's tokens kept (fp32,
+//     by token, part q).
+// k_decode_epilogue -- one 16-column block per workgroup, thread (row block,
+//   lane) = 4 rows of one column.  The splits' partial sums and the h parts
+//   are requested first; meanwhile wave 0 routes the (at most 64) tokens in
+//   LDS (each token's sorted position by comparing keys, then buckets,
+//   modes and tiles from ballots -- the same stable order as the routing
+//   kernel of larger calls) and workgroup 0 publishes the routing.  Then it
+//   adds the parts in a fixed order, adds s * h . B for FUSED buckets (fp32
+//   VALU), rounds once and stores; invalid tokens get NaN.  SEPARATE rows
+//   keep the rounded base for the residual kernel.
 //
 // The fused/separate choice of "LLM 多 LoRA 推理服务工程 2026" (four-layer runtime,
 // execution-unit paragraph) maps to: FUSED = the LoRA term enters the fp32
@@ -49,10 +49,10 @@ namespace lora {
 
 namespace {
 
-constexpr int NWK = 4;            // waves per workgroup of the GEMM kernel (one per SIMD)
-constexpr int DCB = 4;            // 16-column blocks per GEMM workgroup
-constexpr int DCOLS = DCB * 16;   // columns per GEMM workgroup
-constexpr int DSTEPS_PER_WAVE = 8;  // k steps a wave holds at once (per group)
+constexpr int NWK = 4;               // waves per workgroup (one per SIMD)
+constexpr int DCB = 4;               // 16-column blocks per GEMM workgroup
+constexpr int DCOLS = DCB * 16;      // columns per GEMM workgroup
+constexpr int DSTEPS_PER_WAVE = 8;   // k steps a GEMM wave holds at once
 constexpr int SMAX_SEG = DECODE_MAX_T + 2;
 constexpr int SLOT_CAP = MAX_KEYS - 2;
 constexpr int SLOT_LD = SLOT_CAP / (NWK * 64);  // slot-table loads per thread
@@ -83,7 +83,7 @@ struct SmallRoute {
 // token, then each token's sorted position = #(smaller keys) + #(same key,
 // smaller index); buckets, modes, tiles and statistics from ballots.
 // `slot_sr` holds {state, rank} of every slot (LDS).  Other waves return.
-__device__ void small_route(int v, int T, int S, const int2 *slot_sr, int max_rank, int policy, int theta,
+__device__ __forceinline__ void small_route(int v, int T, int S, const int2 *slot_sr, int max_rank, int policy, int theta,
                             SmallRoute &sr) {
     const int lane = threadIdx.x & 63;
     if (threadIdx.x >= 64) return;
@@ -183,7 +183,7 @@ __device__ void small_route(int v, int T, int S, const int2 *slot_sr, int max_ra
 
 // Workgroup 0: publish the routing for the epilogue and residual kernels, the
 // statistics and the invalid-token count.
-__device__ void publish_route(const SmallRoute &sr, int T, const RouteOut &out) {
+__device__ __forceinline__ void publish_route(const SmallRoute &sr, int T, const RouteOut &out) {
     const int tid = threadIdx.x;
     for (int i = tid; i < T; i += blockDim.x) {
         out.perm[i] = sr.perm[i];
@@ -214,13 +214,12 @@ __device__ void publish_route(const SmallRoute &sr, int T, const RouteOut &out) 
 
 template <int DT, int TB, int RB>
 __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_decode_gemm(
-    ApplyArgs a, DecodeArgs d, const int32_t *__restrict__ idx, RouteOut out) {
+    ApplyArgs a, DecodeArgs d, const int32_t *__restrict__ idx) {
     using E = Elem<DT>;
     using V = typename E::vec8;
     constexpr int NB = TB * DCB;  // 16x16 output blocks per wave
+    constexpr int GS = DSTEPS_PER_WAVE;
     __shared__ f32x4_t red[NWK * NB * 64];  // cross-wave sums (64 KiB at TB = 4)
-    __shared__ int2 s_slot[SLOT_CAP];       // {state, rank} per slot (routing workgroups)
-    __shared__ SmallRoute sr;
 
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6);
@@ -235,83 +234,51 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int c0 = cg * DCOLS;
     const int kst = a.d_in >> 5;
     const int qa = q * kst / d.splits;
-    const int nsq = (q + 1) * kst / d.splits - qa;  // k steps of this split
-    const bool routes = cg < d.route_groups;
+    const int nsq = (q + 1) * kst / d.splits - qa;  // k steps of this split (>= 1)
 
-    // 1. Routing inputs first (they return first): the adapter indices and
-    //    every slot's {state, rank}.
-    int v_idx = -1;
-    int2 sl[SLOT_LD];
-    if (routes) {
-        if (tid < T) v_idx = idx[tid];
-#pragma unroll
-        for (int u = 0; u < SLOT_LD; ++u)
-            sl[u] = reinterpret_cast<const int2 *>(a.slots)[2 * min(tid + u * NWK * 64, a.S - 1)];
-    }
-
-    // 2. Wave w takes the split's k steps w, w + 4, ..., w + 28: x fragments
-    //    for all T rows (rows past T repeat row T-1) and W fragments for all
-    //    64 columns, every load unconditional (clamped step).  One wave per
-    //    SIMD holds them all.
-    constexpr int GS = DSTEPS_PER_WAVE;
     // Buffer loads: one per-lane byte offset per operand row; column blocks,
-    // the wave's first step and the per-step stride are uniform (SGPR or
+    // the wave's steps and the per-step stride are uniform (SGPR or
     // immediate offsets), so addressing costs few registers.
     const uint32_t rowb = static_cast<uint32_t>(a.d_in) * 2;  // bytes per row
+    const uint32_t kb = static_cast<uint32_t>(qa) * 64 + 16 * kq;
+    auto step_b = [&](int i) { return static_cast<uint32_t>(min(wave + NWK * i, nsq - 1)) * 64; };
+
+    // 1. Adapter index of token `lane` (every wave holds all T of them), and
+    //    the A fragments of slot cg for this wave's steps.
+    const int my_idx = idx[min(lane, T - 1)];
+    V af[GS][RB];
+    auto load_a = [&](int s) {
+        const __amdgpu_buffer_rsrc_t ars =
+            make_rsrc(static_cast<const uint16_t *>(a.A_slab) + static_cast<size_t>(s) * Rp * a.d_in, Rp * rowb);
+#pragma unroll
+        for (int i = 0; i < GS; ++i)
+#pragma unroll
+            for (int jb = 0; jb < RB; ++jb)
+                af[i][jb] = bload8<V>(ars, static_cast<uint32_t>(min(jb * 16 + r, Rp - 1)) * rowb + kb, step_b(i));
+    };
+    if (cg < a.S) load_a(cg);
+
+    // 2. x fragments for all T rows (rows past T repeat row T-1; their
+    //    outputs are never used) and W fragments for all 64 columns.
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(T) * rowb);
     const __amdgpu_buffer_rsrc_t wrs =
         make_rsrc(static_cast<const uint16_t *>(a.W) + static_cast<size_t>(c0) * a.d_in, DCOLS * rowb);
-    const uint32_t kb = static_cast<uint32_t>(qa) * 64 + 16 * kq;  // byte offset of the lane's k
     uint32_t xo[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) xo[tb] = static_cast<uint32_t>(min(tb * 16 + r, T - 1)) * rowb + kb;
     const uint32_t wo = static_cast<uint32_t>(r) * rowb + kb;
-
-    // All of this wave's operands in flight at once (decode_splits keeps a
-    // split at <= NWK * GS k steps).
     V xf[GS][TB];
     V wf[GS][DCB];
 #pragma unroll
     for (int i = 0; i < GS; ++i) {
-        const uint32_t sb = static_cast<uint32_t>(min(wave + NWK * i, nsq - 1)) * 64;  // uniform
+        const uint32_t sb = step_b(i);
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) xf[i][tb] = bload8<V>(xrs, xo[tb], sb);
 #pragma unroll
         for (int c = 0; c < DCB; ++c) wf[i][c] = bload8<V>(wrs, wo, sb + c * 16 * rowb);
     }
 
-    // 3. Routing in LDS (wave 0), published by workgroup 0.  This
-    //    workgroup's LoRA buckets are g = cg, cg + groups, ...
-    int n_lora = 0;
-    if (routes) {
-#pragma unroll
-        for (int u = 0; u < SLOT_LD; ++u)
-            if (tid + u * NWK * 64 < a.S) s_slot[tid + u * NWK * 64] = sl[u];
-        __syncthreads();
-        small_route(v_idx, T, a.S, s_slot, d.max_rank, a.policy, d.theta, sr);
-        __syncthreads();
-        if (blockIdx.x == 0) publish_route(sr, T, out);
-        n_lora = uniform(sr.n_lora);
-    }
-
-    // 4. A fragments of the first bucket's slot for these steps, issued
-    //    behind x and W so they never delay them.
-    V af[GS][RB];
-    auto load_a = [&](int g) {
-        const int key = uniform(sr.segs[g][0]);
-        const __amdgpu_buffer_rsrc_t ars =
-            make_rsrc(static_cast<const uint16_t *>(a.A_slab) + static_cast<size_t>(key) * Rp * a.d_in, Rp * rowb);
-#pragma unroll
-        for (int i = 0; i < GS; ++i) {
-            const uint32_t sb = static_cast<uint32_t>(min(wave + NWK * i, nsq - 1)) * 64;
-#pragma unroll
-            for (int jb = 0; jb < RB; ++jb)
-                af[i][jb] = bload8<V>(ars, static_cast<uint32_t>(min(jb * 16 + r, Rp - 1)) * rowb + kb, sb);
-        }
-    };
-    if (cg < n_lora) load_a(cg);
-
-    // 5. Base GEMM on the steps this wave holds.
+    // 3. Base GEMM on the steps this wave holds.
     f32x4_t acc[TB][DCB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
@@ -327,37 +294,34 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
     }
 
-    // 6. Cross-wave sums in LDS, fixed order (wave 0 + 1 + 2 + 3), stored
-    //    as this split's partial sums [q][t][c0 .. c0+63], 16 bytes a thread.
+    // 4. The 4 waves' sums in LDS, added in a fixed order (wave 0 + 1 + 2 +
+    //    3), stored as this split's partial sums, fragment order
+    //    [q][16-column block][tb][lane] (16 bytes a lane).
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int c = 0; c < DCB; ++c) red[((wave * TB + tb) * DCB + c) * 64 + lane] = acc[tb][c];
     __syncthreads();
-    float *part = d.part + static_cast<size_t>(q) * T * a.d_out;
-    const float *redf = reinterpret_cast<const float *>(red);
-    for (int e = tid; e < T * (DCOLS / 4); e += NWK * 64) {
-        const int t = e / (DCOLS / 4), c4 = (e % (DCOLS / 4)) * 4;
-        const int tb = t / 16, ii = t % 4, kq2 = (t % 16) / 4;
-        float o[4];
+    f32x4_t *part = reinterpret_cast<f32x4_t *>(d.part);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int col = c4 + u, c = col / 16, ln = kq2 * 16 + col % 16;
-            float sum = 0.0f;
+    for (int f0 = 0; f0 < NB; f0 += NWK) {
+        const int f = f0 + wave;  // fragment (tb, c) = (f / DCB, f % DCB)
+        f32x4_t v = red[f * 64 + lane];
 #pragma unroll
-            for (int w = 0; w < NWK; ++w) sum += redf[(((w * TB + tb) * DCB + c) * 64 + ln) * 4 + ii];
-            o[u] = sum;
-        }
-        *reinterpret_cast<float4 *>(part + static_cast<size_t>(t) * a.d_out + c0 + c4) =
-            float4{o[0], o[1], o[2], o[3]};
+        for (int w = 1; w < NWK; ++w) v += red[(w * NB + f) * 64 + lane];
+        const int tb = f / DCB, c = f % DCB;
+        part[((static_cast<size_t>(q) * (a.d_out / 16) + c0 / 16 + c) * TB + tb) * 64 + lane] = v;
     }
 
-    // 7. Shrink, bucket by bucket: this split's part of h = x . A_slot^T for
-    //    all T rows from the x fragments already held, cross-wave sums in
-    //    LDS, rows of the bucket kept (by sorted row, part q).
+    // 5. Shrink: slots s = cg, cg + ncg, ... named by some token and active.
+    //    This split's part of h for all T rows, from the x fragments held;
+    //    the 4 waves' sums added in order; rows of the slot's tokens kept.
     float *hout = a.h + static_cast<size_t>(q) * T * Rp;
-    for (int g = cg; g < n_lora; g += ncg) {
-        if (g != cg) load_a(g);
+    for (int s = cg; s < a.S; s += ncg) {
+        const unsigned long long mask = __ballot(lane < T && my_idx == s);
+        if (mask == 0) continue;
+        if (uniform(a.slots[s].state) != SLOT_ACTIVE) continue;
+        if (s != cg) load_a(s);
         f32x4_t hacc[TB][RB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
@@ -380,146 +344,179 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int jb = 0; jb < RB; ++jb) red[((wave * TB + tb) * RB + jb) * 64 + lane] = hacc[tb][jb];
         __syncthreads();
-        for (int e = tid; e < T * Rp; e += NWK * 64) {
-            const int t = e / Rp, j = e % Rp;
-            if (sr.tok_seg[t] != g) continue;
-            const int tb = t / 16, ii = t % 4, ln = ((t % 16) / 4) * 16 + (j % 16), jb = j / 16;
-            float sum = 0.0f;
+        for (int f = wave; f < TB * RB; f += NWK) {
+            f32x4_t v = red[f * 64 + lane];
 #pragma unroll
-            for (int w = 0; w < NWK; ++w) sum += redf[(((w * TB + tb) * RB + jb) * 64 + ln) * 4 + ii];
-            hout[static_cast<size_t>(sr.tok_pos[t]) * Rp + j] = sum;
+            for (int w = 1; w < NWK; ++w) v += red[(w * TB * RB + f) * 64 + lane];
+            const int tb = f / RB, j = (f % RB) * 16 + r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = tb * 16 + kq * 4 + i;
+                if (j < Rp && t < T && ((mask >> t) & 1ull)) hout[static_cast<size_t>(t) * Rp + j] = v[i];
+            }
         }
     }
 }
 
 // -------------------------------------------------------------- epilogue --
 
-// Workgroup: 256 threads, 16 columns; thread (t, 4 columns).
-template <int DT, int RB>
-__global__ __launch_bounds__(256) void k_decode_epilogue(ApplyArgs a, DecodeArgs d) {
+// Workgroup: 4 waves, one 16-column block; thread (tb = wave < TB, lane)
+// holds rows tb*16 + 4*(lane/16) + i of column lane % 16.
+template <int DT, int TB, int RB>
+__global__ __launch_bounds__(NWK * 64) void k_decode_epilogue(ApplyArgs a, DecodeArgs d, const int32_t *__restrict__ idx,
+                                                              RouteOut out) {
     using E = Elem<DT>;
     using raw = typename E::raw;
     constexpr int HR = RB * 16;
-    __shared__ float hs[DECODE_MAX_T][HR + 1];
-    __shared__ int s_rec[SMAX_SEG][4];
+    constexpr int TP = TB * 16;
+    constexpr int HQ = (TP * HR / 4 + NWK * 64 - 1) / (NWK * 64);  // h float4s per thread
+    __shared__ float hs[TP][HR + 1];
+    __shared__ int2 s_slot[SLOT_CAP];
+    __shared__ SmallRoute sr;
     const int tid = threadIdx.x;
+    const int wave = uniform(tid >> 6);
+    const int lane = tid & 63;
     const int T = a.T;
     const int Rp = a.R;
-    const int n0 = blockIdx.x * 16;
-    const int t = tid >> 2;
-    const int c4 = (tid & 3) * 4;
-    const int tc = min(t, T - 1);
+    const int nb = blockIdx.x;  // 16-column block
+    const int n = nb * 16 + (lane & 15);
 
-    // Round 1: the splits' partial sums, routing records, h parts.
-    float4 pv[MAX_DSPLIT];
+    // Round 1, all independent: routing inputs, the splits' partial sums,
+    // the h parts.
+    const int v_idx = idx[min(lane, T - 1)];
+    int2 sl[SLOT_LD];
+#pragma unroll
+    for (int u = 0; u < SLOT_LD; ++u)
+        sl[u] = reinterpret_cast<const int2 *>(a.slots)[2 * min(tid + u * NWK * 64, a.S - 1)];
+    const int tb = min(wave, TB - 1);
+    const f32x4_t *part = reinterpret_cast<const f32x4_t *>(d.part) + (static_cast<size_t>(nb) * TB + tb) * 64 + lane;
+    const size_t qstride = static_cast<size_t>(a.d_out / 16) * TB * 64;
+    f32x4_t pv[MAX_DSPLIT];
 #pragma unroll
     for (int qq = 0; qq < MAX_DSPLIT; ++qq)
-        if (qq < d.splits)
-            pv[qq] = *reinterpret_cast<const float4 *>(d.part + (static_cast<size_t>(qq) * T + tc) * a.d_out + n0 + c4);
-    const int seg = a.rv.tok_seg[tc];
-    const int pos = a.rv.tok_pos[tc];
-    const int n_rec = min(T, a.S) + 2;
-    for (int i = tid; i < 4 * n_rec; i += 256) s_rec[i >> 2][i & 3] = a.rv.segs[i];
-    const size_t pstride = static_cast<size_t>(T) * Rp;
-    for (int e = tid; e < T * Rp / 4; e += 256) {
-        float4 hv = reinterpret_cast<const float4 *>(a.h)[e];
-        for (int qq = 1; qq < d.splits; ++qq) {
-            const float4 g = reinterpret_cast<const float4 *>(a.h + qq * pstride)[e];
-            hv.x += g.x;
-            hv.y += g.y;
-            hv.z += g.z;
-            hv.w += g.w;
+        if (qq < d.splits) pv[qq] = part[qq * qstride];
+    const int hq_n = T * Rp / 4;
+    const size_t pstride = static_cast<size_t>(T) * Rp / 4;
+    float4 hv[HQ][MAX_DSPLIT];
+#pragma unroll
+    for (int m = 0; m < HQ; ++m)
+#pragma unroll
+        for (int qq = 0; qq < MAX_DSPLIT; ++qq)
+            if (qq < d.splits)
+                hv[m][qq] = reinterpret_cast<const float4 *>(a.h)[qq * pstride + min(tid + m * NWK * 64, hq_n - 1)];
+
+    // Routing in LDS (wave 0), published by workgroup 0.
+#pragma unroll
+    for (int u = 0; u < SLOT_LD; ++u)
+        if (tid + u * NWK * 64 < a.S) s_slot[tid + u * NWK * 64] = sl[u];
+    __syncthreads();
+    small_route(lane < T ? v_idx : -1, T, a.S, s_slot, d.max_rank, a.policy, d.theta, sr);
+    // h (parts summed in order), by token.
+#pragma unroll
+    for (int m = 0; m < HQ; ++m) {
+        const int e = tid + m * NWK * 64;
+        if (e < hq_n) {
+            float4 v = hv[m][0];
+#pragma unroll
+            for (int qq = 1; qq < MAX_DSPLIT; ++qq) {
+                if (qq < d.splits) {
+                    v.x += hv[m][qq].x;
+                    v.y += hv[m][qq].y;
+                    v.z += hv[m][qq].z;
+                    v.w += hv[m][qq].w;
+                }
+            }
+            const int t = (e * 4) / Rp, j = (e * 4) % Rp;
+            hs[t][j] = v.x;
+            hs[t][j + 1] = v.y;
+            hs[t][j + 2] = v.z;
+            hs[t][j + 3] = v.w;
         }
-        const int p = (e * 4) / Rp, j = (e * 4) % Rp;
-        hs[p][j] = hv.x;
-        hs[p][j + 1] = hv.y;
-        hs[p][j + 2] = hv.z;
-        hs[p][j + 3] = hv.w;
     }
     __syncthreads();
-    if (t >= T) return;
-    float4 acc = pv[0];
+    if (blockIdx.x == 0) publish_route(sr, T, out);
+    if (wave >= TB) return;
+
+    f32x4_t acc = pv[0];
 #pragma unroll
-    for (int qq = 1; qq < MAX_DSPLIT; ++qq) {
-        if (qq < d.splits) {
-            acc.x += pv[qq].x;
-            acc.y += pv[qq].y;
-            acc.z += pv[qq].z;
-            acc.w += pv[qq].w;
+    for (int qq = 1; qq < MAX_DSPLIT; ++qq)
+        if (qq < d.splits) acc += pv[qq];
+    // Round 2, FUSED rows: B rows of their slots and the scales.
+    int key[4];
+    bool fused[4];
+    u32x4_t bw[4][2 * RB];
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = tb * 16 + (lane >> 4) * 4 + i;
+        const int sg = sr.tok_seg[min(t, T - 1)];
+        key[i] = sr.segs[sg][0];
+        fused[i] = t < T && key[i] < a.S && sr.segs[sg][3] == SEG_FUSED;
+        sc[i] = 0.0f;
+        if (fused[i]) {
+            const uint16_t *bp =
+                static_cast<const uint16_t *>(a.B_slab) + (static_cast<size_t>(key[i]) * a.d_out + n) * Rp;
+#pragma unroll
+            for (int qb = 0; qb < 2 * RB; ++qb) bw[i][qb] = *reinterpret_cast<const u32x4_t *>(bp + min(8 * qb, Rp - 8));
+            sc[i] = a.slots[key[i]].scale;
         }
     }
-    float o[4] = {acc.x, acc.y, acc.z, acc.w};
-    const int key = s_rec[seg][0];
-    // Round 2, FUSED rows: s * h . B for the thread's 4 columns.
-    if (key < a.S && s_rec[seg][3] == SEG_FUSED) {
-        u32x4_t bw[4][2 * RB];
+    raw *y = static_cast<raw *>(a.y);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint16_t *bp =
-                static_cast<const uint16_t *>(a.B_slab) + (static_cast<size_t>(key) * a.d_out + n0 + c4 + u) * Rp;
-#pragma unroll
-            for (int qb = 0; qb < 2 * RB; ++qb) bw[u][qb] = *reinterpret_cast<const u32x4_t *>(bp + min(8 * qb, Rp - 8));
-        }
-        const float s = a.slots[key].scale;
-        const float *hrow = hs[pos];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
+    for (int i = 0; i < 4; ++i) {
+        const int t = tb * 16 + (lane >> 4) * 4 + i;
+        if (t >= T) continue;
+        float o = acc[i];
+        if (fused[i]) {
+            const float *hrow = hs[t];
             float dsum = 0.0f;
 #pragma unroll
             for (int qb = 0; qb < 2 * RB; ++qb) {
                 if (8 * qb < Rp) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        dsum += hrow[8 * qb + 2 * e] * E::to_f(static_cast<raw>(bw[u][qb][e] & 0xFFFFu));
-                        dsum += hrow[8 * qb + 2 * e + 1] * E::to_f(static_cast<raw>(bw[u][qb][e] >> 16));
+                        dsum += hrow[8 * qb + 2 * e] * E::to_f(static_cast<raw>(bw[i][qb][e] & 0xFFFFu));
+                        dsum += hrow[8 * qb + 2 * e + 1] * E::to_f(static_cast<raw>(bw[i][qb][e] >> 16));
                     }
                 }
             }
-            o[u] += s * dsum;
+            o += sc[i] * dsum;
         }
+        y[static_cast<size_t>(t) * a.d_out + n] = (key[i] == a.S + 1) ? E::qnan : E::from_f(o);
     }
-    raw ov[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) ov[u] = (key == a.S + 1) ? E::qnan : E::from_f(o[u]);
-    *reinterpret_cast<uint2 *>(static_cast<raw *>(a.y) + static_cast<size_t>(t) * a.d_out + n0 + c4) =
-        uint2{static_cast<uint32_t>(ov[0]) | (static_cast<uint32_t>(ov[1]) << 16),
-              static_cast<uint32_t>(ov[2]) | (static_cast<uint32_t>(ov[3]) << 16)};
 }
 
 template <int DT, int TB>
-hipError_t launch_gemm_tb(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
-                          hipStream_t st, LaunchEvents ev) {
+hipError_t launch_tb(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
+                     hipStream_t st, LaunchEvents ev) {
     const dim3 grid((a.d_out / DCOLS) * d.splits);
+    const dim3 egrid(a.d_out / 16);
     const dim3 block(NWK * 64);
     switch ((a.R + 15) / 16) {
-        case 1: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 1>), grid, block, 0, st, a, d, idx, out); break;
-        case 2: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 2>), grid, block, 0, st, a, d, idx, out); break;
-        case 3: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 3>), grid, block, 0, st, a, d, idx, out); break;
-        default: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 4>), grid, block, 0, st, a, d, idx, out); break;
+        case 1: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 1>), grid, block, 0, st, a, d, idx); break;
+        case 2: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 2>), grid, block, 0, st, a, d, idx); break;
+        case 3: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 3>), grid, block, 0, st, a, d, idx); break;
+        default: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 4>), grid, block, 0, st, a, d, idx); break;
     }
-    return hipGetLastError();
-}
-
-template <int DT>
-hipError_t launch_gemm_dt(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
-                          hipStream_t st, LaunchEvents ev) {
-    switch (decode_token_blocks(a.T)) {
-        case 1: return launch_gemm_tb<DT, 1>(a, d, idx, out, st, ev);
-        case 2: return launch_gemm_tb<DT, 2>(a, d, idx, out, st, ev);
-        default: return launch_gemm_tb<DT, 4>(a, d, idx, out, st, ev);
-    }
-}
-
-template <int DT>
-hipError_t launch_epi_dt(const ApplyArgs &a, const DecodeArgs &d, hipStream_t st) {
-    const dim3 grid(a.d_out / 16);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     switch ((a.R + 15) / 16) {
-        case 1: hipLaunchKernelGGL((k_decode_epilogue<DT, 1>), grid, dim3(256), 0, st, a, d); break;
-        case 2: hipLaunchKernelGGL((k_decode_epilogue<DT, 2>), grid, dim3(256), 0, st, a, d); break;
-        case 3: hipLaunchKernelGGL((k_decode_epilogue<DT, 3>), grid, dim3(256), 0, st, a, d); break;
-        default: hipLaunchKernelGGL((k_decode_epilogue<DT, 4>), grid, dim3(256), 0, st, a, d); break;
+        case 1: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 1>), egrid, block, 0, st, a, d, idx, out); break;
+        case 2: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 2>), egrid, block, 0, st, a, d, idx, out); break;
+        case 3: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 3>), egrid, block, 0, st, a, d, idx, out); break;
+        default: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 4>), egrid, block, 0, st, a, d, idx, out); break;
     }
     return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
+                     hipStream_t st, LaunchEvents ev) {
+    switch (decode_token_blocks(a.T)) {
+        case 1: return launch_tb<DT, 1>(a, d, idx, out, st, ev);
+        case 2: return launch_tb<DT, 2>(a, d, idx, out, st, ev);
+        default: return launch_tb<DT, 4>(a, d, idx, out, st, ev);
+    }
 }
 
 }  // namespace
@@ -531,9 +528,9 @@ int decode_token_blocks(int T) {
 }
 
 int decode_splits(int T, int d_in) {
-    // Every wave holds all its steps: at most NWK x DSTEPS_PER_WAVE k steps
-    // per split, at least 4 splits (64-column workgroups: d_out / 16 of them
-    // at d_out = 4096, one per CU); 0 beyond MAX_DSPLIT splits.
+    // Every GEMM wave holds all its steps: at most NWK x DSTEPS_PER_WAVE k
+    // steps per split, at least 4 splits (64-column workgroups: d_out / 16
+    // of them at d_out = 4096, one per CU); 0 beyond MAX_DSPLIT splits.
     (void)T;
     const int kst = d_in / 32;
     const int per = NWK * DSTEPS_PER_WAVE;
@@ -543,14 +540,10 @@ int decode_splits(int T, int d_in) {
     return s <= MAX_DSPLIT ? s : 0;
 }
 
-hipError_t launch_decode_gemm(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
-                              hipStream_t st, LaunchEvents ev) {
-    return (a.dtype == DT_F16) ? launch_gemm_dt<DT_F16>(a, d, idx, out, st, ev)
-                               : launch_gemm_dt<DT_BF16>(a, d, idx, out, st, ev);
-}
-
-hipError_t launch_decode_epilogue(const ApplyArgs &a, const DecodeArgs &d, hipStream_t st) {
-    return (a.dtype == DT_F16) ? launch_epi_dt<DT_F16>(a, d, st) : launch_epi_dt<DT_BF16>(a, d, st);
+hipError_t launch_decode(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
+                         hipStream_t st, LaunchEvents ev) {
+    return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, d, idx, out, st, ev)
+                               : launch_dt<DT_BF16>(a, d, idx, out, st, ev);
 }
 
 }  // namespace lora

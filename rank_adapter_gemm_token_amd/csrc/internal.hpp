@@ -91,8 +91,9 @@ struct ApplyArgs {
     const void *A_slab; // [S][R][d_in]
     const void *B_slab; // [S][d_out][R]
     const SlotDev *slots;
-    float *h;           // h_parts x [T][R] fp32 by sorted position; h = sum of the parts
+    float *h;           // h_parts x [T][R] fp32; h = sum of the parts
     int h_parts;        // k parts of the shrink, summed in order by the consumers
+    int h_by_token;     // 1: h rows are indexed by token; 0: by sorted position
     RouteView rv;
     int tiles_bound;    // grid bound for tile-parallel kernels
     int policy;         // lora_mode
@@ -117,21 +118,21 @@ struct LaunchEvents {
             hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);                            \
     } while (0)
 
-// Calls of at most DECODE_MAX_T tokens (fp16/bf16): routing, shrink and the
-// split-K base GEMM in one launch (writes `out`, h parts and the partial
-// sums), then the epilogue (split sum, fused expand, rounding, store).
+// Calls of at most DECODE_MAX_T tokens (fp16/bf16), two launches: the
+// split-K base GEMM with the shrink (partial sums and h parts, h by token),
+// then the epilogue, which routes (writes `out`), sums the splits, adds the
+// fused expand, rounds and stores.
 constexpr int DECODE_MAX_T = 64;
 constexpr int MAX_DSPLIT = 16;
 struct DecodeArgs {
     int splits;         // k splits = h parts (decode_splits)
-    int route_groups;   // column groups whose workgroups route (and shrink)
     int max_rank;       // the pool's rank, for the padded-row statistic
     int theta;          // fused threshold
-    float *part;        // fp32 partial sums [splits][T][d_out]
+    float *part;        // fp32 partial sums, [splits][d_out/16][TB][64 lanes] fragments
 };
-hipError_t launch_decode_gemm(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
-                              hipStream_t st, LaunchEvents ev = {});
-hipError_t launch_decode_epilogue(const ApplyArgs &a, const DecodeArgs &d, hipStream_t st);
+// ev (optional) times the GEMM launch.
+hipError_t launch_decode(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
+                         hipStream_t st, LaunchEvents ev = {});
 // k splits of the decode GEMM for (T, d_in); 0 if d_in is too large for it.
 int decode_splits(int T, int d_in);
 int decode_token_blocks(int T);
