@@ -39,6 +39,7 @@ CSRC = os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc")
 KERNELS = {
     "decode": ("k_decode_gemm", ["gemm_decode.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
     "tiled": ("k_gemm_tiled", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
+    "big": ("k_gemm_big", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
 }
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -358,7 +359,15 @@ def main():
             achieved = per_launch / gemm_s / 1e9
             roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS}
-        kind = "decode" if calls[0].T <= 64 else "tiled"
+        c0 = calls[0]
+        # The kernel the library picks for this call shape (gemm_tiled.hip,
+        # gemm_decode.hip).
+        if c0.T <= 64:
+            kind = "decode"
+        elif c0.T >= 2048 and c0.d_out % 256 == 0 and c0.d_in % 128 == 0:
+            kind = "big"
+        else:
+            kind = "tiled"
         roof["kernel"] = KERNELS[kind][0]
         roof["kernel_us"] = gemm_s * 1e6
         roof["traffic"] = traffic_for(args.workload, kind)

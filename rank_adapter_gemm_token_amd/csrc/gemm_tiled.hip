@@ -126,6 +126,115 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
     store_rows<DT, TB, WC>(a, pw, a.T, nw, acc);
 }
 
+// Large calls: 256 x 256 output tile per workgroup of 8 waves (2 x 4, each
+// wave 128 rows x 64 columns: 32 accumulator blocks).  Each 64-wide k stage
+// is 64 fragments (32 of x rows, 32 of W rows); a wave loads 8 of them
+// straight into LDS (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at
+// fragment base + 16 l, which is MFMA fragment order), so operands never
+// pass through registers on the way in.  Two LDS buffers (separate arrays,
+// so the compiler can tell a stage's reads from the next stage's loads):
+// stage s + 1 is loaded while stage s is multiplied, one barrier a stage.
+using lds_ptr = __attribute__((address_space(3))) void *;
+
+template <int DT>
+__global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
+    using E = Elem<DT>;
+    using V = typename E::vec8;
+    constexpr int BM = 256, BN = 256, TB = 8, WC = 4;
+    constexpr int FR = 64;  // fragments per stage
+    __shared__ u32x4_t lds0[FR * 64];
+    __shared__ u32x4_t lds1[FR * 64];
+
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;
+    const int kq = lane >> 4;
+    const int wm = wave >> 2;  // rows wm * 128
+    const int wn = wave & 3;   // columns wn * 64
+    const int m0 = blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN;
+
+    // The 8 fragments this wave loads each stage: f = 8 * wave + i; waves
+    // 0-3 load x fragments (row block f / 2, k half f % 2; rows gathered in
+    // sorted order), waves 4-7 W fragments (column block (f - 32) / 2).
+    // Buffer loads into LDS: the operand's resource (SGPRs), the stage's k
+    // offset as the scalar offset, one 32-bit lane offset per fragment; the
+    // row permutation is read once, in one batch.
+    const bool xw = wave < 4;
+    const __amdgpu_buffer_rsrc_t rs =
+        xw ? make_rsrc(a.x, static_cast<uint32_t>(a.T) * a.d_in * 2)
+           : make_rsrc(a.W, static_cast<uint32_t>(a.d_out) * a.d_in * 2);
+    uint32_t off[8];
+    if (xw) {
+        int tok[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tok[i] = a.rv.perm[min(m0 + ((8 * wave + i) >> 1) * 16 + r, a.T - 1)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            off[i] = static_cast<uint32_t>(min(max(tok[i], 0), a.T - 1)) * (a.d_in * 2) + (i & 1) * 64 + 16 * kq;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            off[i] = static_cast<uint32_t>(n0 + ((8 * wave + i - 32) >> 1) * 16 + r) * (a.d_in * 2) + (i & 1) * 64 +
+                     16 * kq;
+    }
+    auto issue = [&](int s, u32x4_t *buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(buf + (8 * wave + i) * 64), 16, off[i], s * 128, 0,
+                                                     0);
+    };
+
+    f32x4_t acc[TB][WC];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const u32x4_t *buf) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            V bf[WC];
+#pragma unroll
+            for (int wc = 0; wc < WC; ++wc) bf[wc] = __builtin_bit_cast(V, buf[(32 + (wn * WC + wc) * 2 + ks) * 64 + lane]);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const V af = __builtin_bit_cast(V, buf[((wm * TB + tb) * 2 + ks) * 64 + lane]);
+#pragma unroll
+                for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(af, bf[wc], acc[tb][wc]);
+                // One row block at a time: keeps the operands of only a few
+                // blocks live next to the 128 accumulator registers.
+                if (tb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    // Waits for this wave's loads, then for every wave's (the barrier also
+    // means the other buffer is no longer read).
+    auto sync_stage = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    const int nst = a.d_in / 64;  // even: d_in is a multiple of 128 here
+    issue(0, lds0);
+    for (int s = 0; s < nst; s += 2) {
+        sync_stage();
+        issue(s + 1, lds1);
+        compute(lds0);
+        sync_stage();
+        if (s + 2 < nst) issue(s + 2, lds0);
+        compute(lds1);
+    }
+
+    // The epilogue's addresses depend on pw, which the compiler may not
+    // compute before the loop (keeps them from being hoisted and held in
+    // registers across it).
+    int pw = m0 + wm * TB * 16;
+    asm volatile("" : "+s"(pw));
+    const int nw = n0 + wn * WC * 16;
+    lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, acc);
+    store_rows<DT, TB, WC>(a, pw, a.T, nw, acc);
+}
+
 template <int DT, int BM, int BN>
 hipError_t launch_shape(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
     const dim3 grid(a.d_out / BN, (a.T + BM - 1) / BM);
@@ -138,6 +247,11 @@ hipError_t launch_dt(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
     // Large T: 128 x 128 tiles (two workgroups per CU by LDS; a 256 x 256
     // tile needs more than the 256 registers a lane has at that occupancy).
     // Otherwise 64 x 64 tiles, enough of them to fill the chip.
+    if (a.T >= 2048 && a.d_out % 256 == 0 && a.d_in % 128 == 0) {
+        const dim3 grid(a.d_out / 256, (a.T + 255) / 256);
+        LORA_LAUNCH(ev, (k_gemm_big<DT>), grid, dim3(512), 0, st, a);
+        return hipGetLastError();
+    }
     if (a.T >= 512 && a.d_out % 128 == 0) return launch_shape<DT, 128, 128>(a, st, ev);
     return launch_shape<DT, 64, 64>(a, st, ev);
 }
