@@ -127,13 +127,17 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
 }
 
 // Large calls: 256 x 256 output tile per workgroup of 8 waves (2 x 4, each
-// wave 128 rows x 64 columns: 32 accumulator blocks).  Each 64-wide k stage
-// is 64 fragments (32 of x rows, 32 of W rows); a wave loads 8 of them
-// straight into LDS (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at
-// fragment base + 16 l, which is MFMA fragment order), so operands never
-// pass through registers on the way in.  Two LDS buffers (separate arrays,
-// so the compiler can tell a stage's reads from the next stage's loads):
-// stage s + 1 is loaded while stage s is multiplied, one barrier a stage.
+// wave 128 rows x 64 columns: 32 accumulator blocks).  A 64-wide k stage is
+// 16 row blocks of x and 16 of W, each 16 rows x 128 bytes (2 KiB) in LDS.
+// Operands go straight from global memory into LDS (buffer_load_dwordx4 ...
+// lds: lane l's 16 bytes land at instruction base + 16 l), one instruction
+// per 8 rows, 8 lanes covering each row's whole 128-byte line.  Which
+// 16-byte chunk a lane fetches is XOR-swizzled by row, so the chunk stored
+// in position m of row rho is chunk m ^ sw(rho), sw(rho) = (rho & 7) ^
+// (rho >> 3); the MFMA operand reads (16 rows of one chunk at a time) then
+// hit distinct banks.  Two LDS buffers (separate arrays, so the compiler
+// can tell a stage's reads from the next stage's loads): stage s + 1 is
+// loaded while stage s is multiplied, one barrier a stage.
 using lds_ptr = __attribute__((address_space(3))) void *;
 
 template <int DT>
@@ -141,49 +145,64 @@ __global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
     using E = Elem<DT>;
     using V = typename E::vec8;
     constexpr int BM = 256, BN = 256, TB = 8, WC = 4;
-    constexpr int FR = 64;  // fragments per stage
-    __shared__ u32x4_t lds0[FR * 64];
-    __shared__ u32x4_t lds1[FR * 64];
+    constexpr int RBU = 128;             // 16-byte units per row block (16 rows x 128 B)
+    constexpr int BOFF = 16 * RBU;       // W row blocks follow the 16 x row blocks
+    __shared__ u32x4_t lds0[32 * RBU];   // 64 KiB
+    __shared__ u32x4_t lds1[32 * RBU];
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
-    const int kq = lane >> 4;
+    const int g = lane >> 4;
     const int wm = wave >> 2;  // rows wm * 128
     const int wn = wave & 3;   // columns wn * 64
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
 
-    // The 8 fragments this wave loads each stage: f = 8 * wave + i; waves
-    // 0-3 load x fragments (row block f / 2, k half f % 2; rows gathered in
-    // sorted order), waves 4-7 W fragments (column block (f - 32) / 2).
-    // Buffer loads into LDS: the operand's resource (SGPRs), the stage's k
-    // offset as the scalar offset, one 32-bit lane offset per fragment; the
-    // row permutation is read once, in one batch.
+    // Loads: wave w < 4 fetches x row blocks 4w .. 4w+3, wave w >= 4 W row
+    // blocks 4(w-4) .. +3; instruction i covers row block 4(w%4) + i/2, rows
+    // 8 (i&1) + lane/8, chunk (lane&7) ^ sw(row).  Buffer loads into LDS:
+    // the operand's resource in SGPRs, the stage's k offset as the scalar
+    // offset, one 32-bit lane offset per instruction; the row permutation is
+    // read once, in one batch.
     const bool xw = wave < 4;
     const __amdgpu_buffer_rsrc_t rs =
         xw ? make_rsrc(a.x, static_cast<uint32_t>(a.T) * a.d_in * 2)
            : make_rsrc(a.W, static_cast<uint32_t>(a.d_out) * a.d_in * 2);
+    const int lrow = lane >> 3;                      // row within the 8-row half
     uint32_t off[8];
+    int rowi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rowi[i] = (4 * (wave & 3) + (i >> 1)) * 16 + 8 * (i & 1) + lrow;  // row in tile
     if (xw) {
         int tok[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tok[i] = a.rv.perm[min(m0 + ((8 * wave + i) >> 1) * 16 + r, a.T - 1)];
+        for (int i = 0; i < 8; ++i) tok[i] = a.rv.perm[min(m0 + rowi[i], a.T - 1)];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            off[i] = static_cast<uint32_t>(min(max(tok[i], 0), a.T - 1)) * (a.d_in * 2) + (i & 1) * 64 + 16 * kq;
+        for (int i = 0; i < 8; ++i) rowi[i] = min(max(tok[i], 0), a.T - 1);
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            off[i] = static_cast<uint32_t>(n0 + ((8 * wave + i - 32) >> 1) * 16 + r) * (a.d_in * 2) + (i & 1) * 64 +
-                     16 * kq;
+        for (int i = 0; i < 8; ++i) rowi[i] += n0;
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rho = 8 * (i & 1) + lrow;  // row within its block
+        const int chunk = (lane & 7) ^ (rho & 7) ^ (rho >> 3);
+        off[i] = static_cast<uint32_t>(rowi[i]) * (a.d_in * 2) + chunk * 16;
+    }
+    const int ldsbase = (xw ? 0 : BOFF) + 4 * (wave & 3) * RBU;  // first row block this wave fills
     auto issue = [&](int s, u32x4_t *buf) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(buf + (8 * wave + i) * 64), 16, off[i], s * 128, 0,
-                                                     0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(buf + ldsbase + (i >> 1) * RBU + (i & 1) * 64), 16,
+                                                     off[i], s * 128, 0, 0);
     };
+
+    // Operand reads: lane (r, g) of k step ks takes row r, chunk 4 ks + g,
+    // stored at position (4 ks + g) ^ sw(r) of the row.
+    const int sw = (r & 7) ^ (r >> 3);
+    const int lo0 = r * 8 + ((0 + g) ^ sw);
+    const int lo1 = r * 8 + ((4 + g) ^ sw);
 
     f32x4_t acc[TB][WC];
 #pragma unroll
@@ -193,12 +212,13 @@ __global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
     auto compute = [&](const u32x4_t *buf) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            const int lo = ks ? lo1 : lo0;
             V bf[WC];
 #pragma unroll
-            for (int wc = 0; wc < WC; ++wc) bf[wc] = __builtin_bit_cast(V, buf[(32 + (wn * WC + wc) * 2 + ks) * 64 + lane]);
+            for (int wc = 0; wc < WC; ++wc) bf[wc] = __builtin_bit_cast(V, buf[BOFF + (wn * WC + wc) * RBU + lo]);
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
-                const V af = __builtin_bit_cast(V, buf[((wm * TB + tb) * 2 + ks) * 64 + lane]);
+                const V af = __builtin_bit_cast(V, buf[(wm * TB + tb) * RBU + lo]);
 #pragma unroll
                 for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(af, bf[wc], acc[tb][wc]);
                 // One row block at a time: keeps the operands of only a few
