@@ -243,7 +243,16 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     const size_t h_rows = std::max(T, static_cast<size_t>(dec_splits) * dec_T);
     const size_t o_h = take(h_rows * Rp * 4);
     const size_t dec_rows = static_cast<size_t>(lora::decode_token_blocks(static_cast<int>(dec_T))) * 16;
-    const size_t o_part = take(static_cast<size_t>(dec_splits) * dec_rows * d_out * 4);
+    // Split-K partial sums of calls of 65 .. 2047 tokens: the largest
+    // splits x rows over the token counts the pool accepts.
+    size_t tiled_part = 0;
+    if (esz == 2)
+        for (int t = lora::DECODE_MAX_T + 1; t <= max_tokens && t < 2048; t += 16) {
+            const int tl = std::min(t + 15, std::min(max_tokens, 2047));
+            const size_t need = static_cast<size_t>(lora::tiled_splits(tl, d_in, d_out)) * ((tl + 15) / 16 * 16) * d_out;
+            tiled_part = std::max(tiled_part, need);
+        }
+    const size_t o_part = take(std::max(static_cast<size_t>(dec_splits) * dec_rows * d_out, tiled_part) * 4);
     const size_t ws_bytes = off;
 
     e = hipMalloc(&p->A_slab, a_bytes);
@@ -428,7 +437,7 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
         if (half) {
-            HIP_TRY(lora::launch_gemm_tiled(a, st, kev));
+            HIP_TRY(lora::launch_gemm_tiled(a, p->part, st, kev));
         } else {
             HIP_TRY(lora::launch_base_gemm(a, st));
             HIP_TRY(mark(5));

@@ -126,54 +126,70 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
     store_rows<DT, TB, WC>(a, pw, a.T, nw, acc);
 }
 
-// Large calls: 256 x 256 output tile per workgroup of 8 waves (2 x 4, each
-// wave 128 rows x 64 columns: 32 accumulator blocks).  A 64-wide k stage is
-// 16 row blocks of x and 16 of W, each 16 rows x 128 bytes (2 KiB) in LDS.
-// Operands go straight from global memory into LDS (buffer_load_dwordx4 ...
-// lds: lane l's 16 bytes land at instruction base + 16 l), one instruction
-// per 8 rows, 8 lanes covering each row's whole 128-byte line.  Which
-// 16-byte chunk a lane fetches is XOR-swizzled by row, so the chunk stored
-// in position m of row rho is chunk m ^ sw(rho), sw(rho) = (rho & 7) ^
-// (rho >> 3); the MFMA operand reads (16 rows of one chunk at a time) then
-// hit distinct banks.  Two LDS buffers (separate arrays, so the compiler
-// can tell a stage's reads from the next stage's loads): stage s + 1 is
-// loaded while stage s is multiplied, one barrier a stage.
+// 256-row tiles, operands straight into LDS.  A workgroup of 8 waves (2 x
+// 4) computes a 256 x BN output tile (BN = 256: each wave 128 rows x 64
+// columns; BN = 128: 128 x 32) over a range of k stages.  A 64-wide k stage
+// is 16 row blocks of x and BN/16 of W, each 16 rows x 128 bytes (2 KiB) in
+// LDS.  Operands go from global memory into LDS directly (buffer_load_dwordx4
+// ... lds: lane l's 16 bytes land at instruction base + 16 l), one
+// instruction per 8 rows, 8 lanes covering each row's whole 128-byte line.
+// Which 16-byte chunk a lane fetches is XOR-swizzled by row, so the chunk in
+// position m of row rho is chunk m ^ sw(rho), sw(rho) = (rho & 7) ^ (rho >>
+// 3); the MFMA operand reads (16 rows of one chunk at a time) then hit
+// distinct banks.  Two LDS buffers (separate arrays, so the compiler can tell
+// a stage's reads from the next stage's loads): stage s + 1 is loaded while
+// stage s is multiplied, one barrier a stage.
+//
+// SPLIT = false (calls of >= 2048 tokens): all of d_in, then the fused
+// expand and the scatter to token order in the epilogue.
+// SPLIT = true (calls of 65 .. 2047 tokens, too few 256-row tiles to fill
+// the chip): workgroup z of the grid's third dimension takes the z-th of
+// gridDim.z k ranges and stores fp32 partial sums in MFMA fragment order;
+// k_split_epilogue adds them.
 using lds_ptr = __attribute__((address_space(3))) void *;
 
-template <int DT>
-__global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
+template <int DT, int BN, bool SPLIT>
+__global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     using E = Elem<DT>;
     using V = typename E::vec8;
-    constexpr int BM = 256, BN = 256, TB = 8, WC = 4;
+    constexpr int BM = 256, TB = 8, WC = BN / 64;
     constexpr int RBU = 128;             // 16-byte units per row block (16 rows x 128 B)
     constexpr int BOFF = 16 * RBU;       // W row blocks follow the 16 x row blocks
-    __shared__ u32x4_t lds0[32 * RBU];   // 64 KiB
-    __shared__ u32x4_t lds1[32 * RBU];
+    constexpr int NBW = BN / 16;         // W row blocks per stage
+    constexpr int BLD = NBW / 2;         // W load instructions per W wave (4 waves)
+    __shared__ u32x4_t lds0[(16 + NBW) * RBU];
+    __shared__ u32x4_t lds1[(16 + NBW) * RBU];
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int g = lane >> 4;
     const int wm = wave >> 2;  // rows wm * 128
-    const int wn = wave & 3;   // columns wn * 64
+    const int wn = wave & 3;   // columns wn * BN / 4
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
+    const int nst_all = a.d_in / 64;
+    const int s_beg = SPLIT ? uniform(static_cast<int>(blockIdx.z) * nst_all / static_cast<int>(gridDim.z)) : 0;
+    const int s_end = SPLIT ? uniform((static_cast<int>(blockIdx.z) + 1) * nst_all / static_cast<int>(gridDim.z))
+                            : nst_all;
 
-    // Loads: wave w < 4 fetches x row blocks 4w .. 4w+3, wave w >= 4 W row
-    // blocks 4(w-4) .. +3; instruction i covers row block 4(w%4) + i/2, rows
-    // 8 (i&1) + lane/8, chunk (lane&7) ^ sw(row).  Buffer loads into LDS:
-    // the operand's resource in SGPRs, the stage's k offset as the scalar
-    // offset, one 32-bit lane offset per instruction; the row permutation is
-    // read once, in one batch.
+    // Loads: wave w < 4 fetches x row blocks 4w .. 4w+3 (8 instructions),
+    // wave w >= 4 W row blocks (BLD instructions); instruction i covers row
+    // block (first + i/2), rows 8 (i&1) + lane/8, chunk (lane&7) ^ sw(row).
+    // Buffer loads into LDS: the operand's resource in SGPRs, the stage's k
+    // offset as the scalar offset, one 32-bit lane offset per instruction;
+    // the row permutation is read once, in one batch.
     const bool xw = wave < 4;
+    const int nld = xw ? 8 : BLD;
     const __amdgpu_buffer_rsrc_t rs =
         xw ? make_rsrc(a.x, static_cast<uint32_t>(a.T) * a.d_in * 2)
            : make_rsrc(a.W, static_cast<uint32_t>(a.d_out) * a.d_in * 2);
-    const int lrow = lane >> 3;                      // row within the 8-row half
+    const int lrow = lane >> 3;  // row within the 8-row half
+    const int rb0 = (wave & 3) * (xw ? 4 : BLD / 2);  // first row block this wave fills
     uint32_t off[8];
     int rowi[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rowi[i] = (4 * (wave & 3) + (i >> 1)) * 16 + 8 * (i & 1) + lrow;  // row in tile
+    for (int i = 0; i < 8; ++i) rowi[i] = (rb0 + (i >> 1)) * 16 + 8 * (i & 1) + lrow;  // row in tile
     if (xw) {
         int tok[8];
 #pragma unroll
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
         for (int i = 0; i < 8; ++i) rowi[i] = min(max(tok[i], 0), a.T - 1);
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rowi[i] += n0;
+        for (int i = 0; i < 8; ++i) rowi[i] = min(n0 + rowi[i], a.d_out - 1);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -190,12 +206,13 @@ __global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
         const int chunk = (lane & 7) ^ (rho & 7) ^ (rho >> 3);
         off[i] = static_cast<uint32_t>(rowi[i]) * (a.d_in * 2) + chunk * 16;
     }
-    const int ldsbase = (xw ? 0 : BOFF) + 4 * (wave & 3) * RBU;  // first row block this wave fills
+    const int ldsbase = (xw ? 0 : BOFF) + rb0 * RBU;
     auto issue = [&](int s, u32x4_t *buf) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(buf + ldsbase + (i >> 1) * RBU + (i & 1) * 64), 16,
-                                                     off[i], s * 128, 0, 0);
+            if (i < nld)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(buf + ldsbase + (i >> 1) * RBU + (i & 1) * 64),
+                                                         16, off[i], s * 128, 0, 0);
     };
 
     // Operand reads: lane (r, g) of k step ks takes row r, chunk 4 ks + g,
@@ -222,7 +239,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
 #pragma unroll
                 for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(af, bf[wc], acc[tb][wc]);
                 // One row block at a time: keeps the operands of only a few
-                // blocks live next to the 128 accumulator registers.
+                // blocks live next to the accumulators.
                 if (tb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -234,15 +251,17 @@ __global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
         __syncthreads();
     };
 
-    const int nst = a.d_in / 64;  // even: d_in is a multiple of 128 here
-    issue(0, lds0);
-    for (int s = 0; s < nst; s += 2) {
+    const int nst = s_end - s_beg;
+    issue(s_beg, lds0);
+    for (int j = 0; j < nst; j += 2) {
         sync_stage();
-        issue(s + 1, lds1);
+        if (j + 1 < nst) issue(s_beg + j + 1, lds1);
         compute(lds0);
-        sync_stage();
-        if (s + 2 < nst) issue(s + 2, lds0);
-        compute(lds1);
+        if (j + 1 < nst) {
+            sync_stage();
+            if (j + 2 < nst) issue(s_beg + j + 2, lds0);
+            compute(lds1);
+        }
     }
 
     // The epilogue's addresses depend on pw, which the compiler may not
@@ -251,8 +270,56 @@ __global__ __launch_bounds__(512) void k_gemm_big(ApplyArgs a) {
     int pw = m0 + wm * TB * 16;
     asm volatile("" : "+s"(pw));
     const int nw = n0 + wn * WC * 16;
-    lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, acc);
-    store_rows<DT, TB, WC>(a, pw, a.T, nw, acc);
+    if (!SPLIT) {
+        lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, acc);
+        store_rows<DT, TB, WC>(a, pw, a.T, nw, acc);
+    } else {
+        // Partial sums [z][16-row block][16-column block][lane], row blocks
+        // of sorted rows below T only.
+        const int nrb = (a.T + 15) / 16, ncb = a.d_out / 16;
+        f32x4_t *pz = reinterpret_cast<f32x4_t *>(part) + static_cast<size_t>(blockIdx.z) * nrb * ncb * 64;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int rb = pw / 16 + tb;
+            if (rb < nrb) {
+#pragma unroll
+                for (int wc = 0; wc < WC; ++wc)
+                    pz[(static_cast<size_t>(rb) * ncb + nw / 16 + wc) * 64 + lane] = acc[tb][wc];
+            }
+        }
+    }
+}
+
+// Split sums of k_gemm_lds<.., true>: workgroup of 4 waves over 64 sorted rows
+// x 64 columns, wave w = rows (4 blockIdx.y + w) * 16 .. +15.  Adds the
+// splits' partial sums in a fixed order, then the fused expand and the
+// scatter to token order, as the unsplit kernel's epilogue does.
+template <int DT>
+__global__ __launch_bounds__(256) void k_split_epilogue(ApplyArgs a, const float *part, int splits) {
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int rb = static_cast<int>(blockIdx.y) * 4 + wave;
+    const int nrb = (a.T + 15) / 16, ncb = a.d_out / 16;
+    if (rb >= nrb) return;
+    const int cb0 = static_cast<int>(blockIdx.x) * 4;
+    const f32x4_t *p = reinterpret_cast<const f32x4_t *>(part) + (static_cast<size_t>(rb) * ncb + cb0) * 64 + lane;
+    const size_t zs = static_cast<size_t>(nrb) * ncb * 64;
+    f32x4_t v[MAX_TSPLIT][4];
+#pragma unroll
+    for (int z = 0; z < MAX_TSPLIT; ++z)
+        if (z < splits)
+#pragma unroll
+            for (int wc = 0; wc < 4; ++wc) v[z][wc] = p[z * zs + wc * 64];
+    f32x4_t acc[1][4];
+#pragma unroll
+    for (int wc = 0; wc < 4; ++wc) {
+        acc[0][wc] = v[0][wc];
+#pragma unroll
+        for (int z = 1; z < MAX_TSPLIT; ++z)
+            if (z < splits) acc[0][wc] += v[z][wc];
+    }
+    lora_expand_mfma<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, SEG_FUSED, acc);
+    store_rows<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, acc);
 }
 
 template <int DT, int BM, int BN>
@@ -263,13 +330,20 @@ hipError_t launch_shape(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
 }
 
 template <int DT>
-hipError_t launch_dt(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
-    // Large T: 128 x 128 tiles (two workgroups per CU by LDS; a 256 x 256
-    // tile needs more than the 256 registers a lane has at that occupancy).
-    // Otherwise 64 x 64 tiles, enough of them to fill the chip.
+hipError_t launch_dt(const ApplyArgs &a, float *part, hipStream_t st, LaunchEvents ev) {
     if (a.T >= 2048 && a.d_out % 256 == 0 && a.d_in % 128 == 0) {
         const dim3 grid(a.d_out / 256, (a.T + 255) / 256);
-        LORA_LAUNCH(ev, (k_gemm_big<DT>), grid, dim3(512), 0, st, a);
+        LORA_LAUNCH(ev, (k_gemm_lds<DT, 256, false>), grid, dim3(512), 0, st, a, nullptr);
+        return hipGetLastError();
+    }
+    const int splits = tiled_splits(a.T, a.d_in, a.d_out);
+    if (splits > 0) {
+        const dim3 grid(a.d_out / 128, (a.T + 255) / 256, splits);
+        LORA_LAUNCH(ev, (k_gemm_lds<DT, 128, true>), grid, dim3(512), 0, st, a, part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const dim3 egrid(a.d_out / 64, (a.T + 63) / 64);
+        hipLaunchKernelGGL((k_split_epilogue<DT>), egrid, dim3(256), 0, st, a, part, splits);
         return hipGetLastError();
     }
     if (a.T >= 512 && a.d_out % 128 == 0) return launch_shape<DT, 128, 128>(a, st, ev);
@@ -278,8 +352,20 @@ hipError_t launch_dt(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
 
 }  // namespace
 
-hipError_t launch_gemm_tiled(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
-    return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, st, ev) : launch_dt<DT_BF16>(a, st, ev);
+int tiled_splits(int T, int d_in, int d_out) {
+    // Split-K for calls of 65 .. 2047 tokens: 256 x 128 tiles, the smallest
+    // power-of-two split (<= MAX_TSPLIT) that gives >= 256 workgroups with
+    // at least 4 k stages each; 0 when the shape does not fit the kernel
+    // (then the register-staged tiles run unsplit).
+    if (T <= DECODE_MAX_T || T >= 2048 || d_out % 128 != 0 || d_in % 128 != 0) return 0;
+    const int tiles = (d_out / 128) * ((T + 255) / 256);
+    int s = 1;
+    while (s < MAX_TSPLIT && tiles * s < 256 && d_in / 64 >= 8 * s) s *= 2;
+    return s;
+}
+
+hipError_t launch_gemm_tiled(const ApplyArgs &a, float *part, hipStream_t st, LaunchEvents ev) {
+    return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, part, st, ev) : launch_dt<DT_BF16>(a, part, st, ev);
 }
 
 }  // namespace lora

@@ -137,7 +137,11 @@ hipError_t launch_decode(const ApplyArgs &a, const DecodeArgs &d, const int32_t 
 int decode_splits(int T, int d_in);
 int decode_token_blocks(int T);
 // Larger calls (fp16/bf16): LDS-tiled MFMA GEMM with the fused expand.
-hipError_t launch_gemm_tiled(const ApplyArgs &a, hipStream_t st, LaunchEvents ev = {});
+// Calls of 65 .. 2047 tokens may split k (tiled_splits > 0): `part` then
+// holds splits x ceil(T/16)*16 x d_out fp32 partial sums.
+constexpr int MAX_TSPLIT = 8;
+int tiled_splits(int T, int d_in, int d_out);
+hipError_t launch_gemm_tiled(const ApplyArgs &a, float *part, hipStream_t st, LaunchEvents ev = {});
 // fp32 pools: VALU base GEMM and residual expand.
 hipError_t launch_base_gemm(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_expand_separate(const ApplyArgs &a, hipStream_t st);

@@ -80,9 +80,14 @@ def _small_case(dtype, T, d_in, d_out, S, R, seed):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+# Shapes reach every base-GEMM variant: split-K decode (T <= 64), the
+# register-staged tiles (ragged d_in / d_out), the split-K 256-row tiles
+# (T 65 .. 2047 with d_in, d_out multiples of 128; 4 and 2 splits here) and
+# the unsplit 256 x 256 tiles (T >= 2048), each with a ragged last tile.
 @pytest.mark.parametrize("T,d_in,d_out,S,R", [(1, 64, 64, 1, 1), (37, 128, 192, 5, 8),
                                                (77, 192, 128, 9, 16), (300, 256, 320, 17, 64),
-                                               (513, 64, 128, 40, 24)])
+                                               (513, 64, 128, 40, 24), (200, 1024, 384, 7, 16),
+                                               (1000, 512, 512, 11, 32), (2100, 256, 256, 3, 8)])
 @pytest.mark.parametrize("policy", [0, 1, 2])
 def test_small_ragged_full(dtype, T, d_in, d_out, S, R, policy):
     x, W, ads, idx = _small_case(dtype, T, d_in, d_out, S, R, seed=T * 31 + S)
