@@ -136,16 +136,59 @@ __device__ __forceinline__ void load_h8(const ApplyArgs &a, int p, int j, float 
     hv[4] = h1.x; hv[5] = h1.y; hv[6] = h1.z; hv[7] = h1.w;
 }
 
+// Routing facts of a wave tile's rows, one row per lane: lane r holds row
+// p0 + 16 tb + r of each of the TB row blocks (lanes 16..63 repeat lanes
+// 0..15).  g is the bucket record (-1 for rows past rows_end), tok the token,
+// key / mode the bucket's slot and mode, s the slot's scale.  Three batched
+// rounds of loads for all TB blocks at once.
+template <int TB>
+struct RowFacts {
+    int g[TB];
+    int tok[TB];
+    int key[TB];
+    int mode[TB];
+    float s[TB];
+};
+
+template <int TB>
+__device__ __forceinline__ void row_facts(const ApplyArgs &a, int p0, int rows_end, RowFacts<TB> &f) {
+    const int r = threadIdx.x & 15;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int pc = min(p0 + tb * 16 + r, rows_end - 1);
+        f.g[tb] = a.rv.pos_seg[pc];
+        f.tok[tb] = min(max(a.rv.perm[pc], 0), a.T - 1);
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        f.key[tb] = a.rv.segs[4 * f.g[tb]];
+        f.mode[tb] = a.rv.segs[4 * f.g[tb] + 3];
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) f.s[tb] = a.slots[min(f.key[tb], a.S - 1)].scale;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+        if (p0 + tb * 16 + r >= rows_end) f.g[tb] = -1;
+}
+
 // Adds s_g * h[p][:] . B_g[n][:] to acc for every row p of the wave tile whose
 // bucket g has mode `want` (FUSED inside the base GEMM, SEPARATE in the
 // residual kernel).  The wave tile is TB blocks of 16 sorted rows starting at
-// row p0, and WC blocks of 16 columns starting at column n0.  rows_end bounds
-// the rows considered (T, or the end of one bucket tile).
+// row p0, and WC blocks of 16 columns starting at column n0; rows_end bounds
+// the rows considered (T, or the end of one bucket tile); f holds the rows'
+// routing facts.  A block's H operand is s * h rounded to the pool dtype
+// (zero for other rows); the h rows of the next block are requested while
+// the current one is multiplied.  When one bucket covers the whole tile (the
+// usual case for long buckets) its B fragments are loaded once; otherwise
+// each block meets its buckets one at a time (rows are sorted, so a bucket
+// is a run of lanes), one round of B loads per bucket.
 template <int DT, int TB, int WC>
 __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int rows_end, int n0, int want,
-                                                 f32x4_t (&acc)[TB][WC]) {
+                                                 const RowFacts<TB> &f, f32x4_t (&acc)[TB][WC]) {
     using E = Elem<DT>;
     using V = typename E::vec8;
+    using raw = typename E::raw;
+    constexpr int JM = 2;  // 32-wide rank steps (Rp <= 64)
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int kq = lane >> 4;
@@ -153,47 +196,98 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
     p0 = uniform(p0);
     rows_end = uniform(rows_end);
     n0 = uniform(n0);
+
+    bool any_row = false;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) any_row = any_row || (f.g[tb] >= 0 && f.key[tb] < a.S && f.mode[tb] == want);
+    if (__ballot(any_row) == 0) return;
+
+    // Raw h of block tb's rows for rank step js (unconditional loads:
+    // clamped row and rank).
+    auto load_h = [&](int tb, int js, float (&hv)[8]) {
+        const int hrow = a.h_by_token ? f.tok[tb] : min(p0 + tb * 16 + r, rows_end - 1);
+        load_h8(a, hrow, min(js * 32 + 8 * kq, Rp - 8), hv);
+    };
+    // H operand of block tb, rank step js, for bucket gg (-1: any bucket of
+    // mode `want`).
+    auto make_h = [&](int tb, int js, int gg, const float (&hv)[8]) {
+        const bool lr = f.g[tb] >= 0 && f.key[tb] < a.S && f.mode[tb] == want && (gg < 0 || f.g[tb] == gg);
+        raw hr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hr[e] = E::from_f(f.s[tb] * hv[e]);
+        return (lr && js * 32 + 8 * kq < Rp) ? __builtin_bit_cast(V, hr) : zero8<V>();
+    };
+    auto load_b = [&](int key, int js, V (&bf)[WC]) {
+        const int j = min(js * 32 + 8 * kq, Rp - 8);
+        const uint16_t *bp =
+            static_cast<const uint16_t *>(a.B_slab) + (static_cast<size_t>(key) * a.d_out + n0 + r) * Rp + j;
+#pragma unroll
+        for (int wc = 0; wc < WC; ++wc) bf[wc] = load8<V>(bp + static_cast<size_t>(wc) * 16 * Rp);
+    };
+
+    // One bucket over the whole tile?
+    const int g_first = uniform(f.g[0]);
+    bool other = false;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) other = other || (f.g[tb] >= 0 && f.g[tb] != g_first);
+    if (__ballot(other) == 0) {
+        const int key = uniform(f.key[0]);
+#pragma unroll
+        for (int js = 0; js < JM; ++js) {
+            if (js * 32 >= Rp) break;
+            V bf[WC];
+            load_b(key, js, bf);
+            float hv[2][8];
+            load_h(0, js, hv[0]);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                if (p0 + tb * 16 >= rows_end) break;
+                if (tb + 1 < TB) load_h(tb + 1, js, hv[(tb + 1) & 1]);  // next block's rows in flight
+                const V h = make_h(tb, js, -1, hv[tb & 1]);
+#pragma unroll
+                for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(h, bf[wc], acc[tb][wc]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        return;
+    }
+    // Otherwise block by block, bucket by bucket.
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const int pb = p0 + tb * 16;
         if (pb >= rows_end) break;
-        const int g0 = uniform(a.rv.pos_seg[pb]);
-        const int g1 = uniform(a.rv.pos_seg[min(pb + 15, rows_end - 1)]);
-        const int ph = pb + r;  // this lane's row in the H operand
-        const int gh = (ph < rows_end) ? a.rv.pos_seg[ph] : -1;
-        for (int g = g0; g <= g1; ++g) {
-            const int key = uniform(a.rv.segs[4 * g]);
-            const int mode = uniform(a.rv.segs[4 * g + 3]);
+        float hv[JM][8];
+#pragma unroll
+        for (int js = 0; js < JM; ++js) load_h(tb, js, hv[js]);
+        const int last = min(15, rows_end - 1 - pb);
+        const int g0 = uniform(f.g[tb]);
+        const int g1 = __builtin_amdgcn_readlane(f.g[tb], last);
+        for (int gg = g0; gg <= g1; ++gg) {
+            const unsigned long long m = __ballot(f.g[tb] == gg) & 0xFFFFull;
+            if (m == 0) continue;
+            const int l0 = __ffsll(static_cast<long long>(m)) - 1;
+            const int key = __builtin_amdgcn_readlane(f.key[tb], l0);
+            const int mode = __builtin_amdgcn_readlane(f.mode[tb], l0);
             if (key >= a.S || mode != want) continue;
-            const float s = a.slots[key].scale;
-            for (int js = 0; js < Rp; js += 32) {
-                const int j = js + 8 * kq;
-                const bool jv = j < Rp;
-                V hf = zero8<V>();
-                if (jv && gh == g) {
-                    float hv[8];
-                    load_h8(a, a.h_by_token ? token_of(a, ph) : ph, j, hv);
-                    typename E::raw hr[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) hr[e] = E::from_f(s * hv[e]);
-                    hf = __builtin_bit_cast(V, hr);
-                }
-                const uint16_t *bp = static_cast<const uint16_t *>(a.B_slab) +
-                                     (static_cast<size_t>(key) * a.d_out + n0 + r) * Rp + j;
+            for (int js = 0; js < JM; ++js) {
+                if (js * 32 >= Rp) break;
+                V bf[WC];
+                load_b(key, js, bf);
+                const V h = make_h(tb, js, gg, hv[js]);
 #pragma unroll
-                for (int wc = 0; wc < WC; ++wc) {
-                    const V bf = jv ? load8<V>(bp + static_cast<size_t>(wc) * 16 * Rp) : zero8<V>();
-                    acc[tb][wc] = E::mfma(hf, bf, acc[tb][wc]);
-                }
+                for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(h, bf[wc], acc[tb][wc]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // Round and store the wave tile's rows (sorted rows p0 + ...) to y in token
-// order; invalid tokens get NaN.
+// order; invalid tokens get NaN.  The accumulator row 16 tb + 4 kq + i of a
+// lane is row 4 kq + i of block tb, whose facts lane 4 kq + i holds.
 template <int DT, int TB, int WC>
-__device__ __forceinline__ void store_rows(const ApplyArgs &a, int p0, int rows_end, int n0,
+__device__ __forceinline__ void store_rows(const ApplyArgs &a, int p0, int rows_end, int n0, const RowFacts<TB> &f,
                                            const f32x4_t (&acc)[TB][WC]) {
     using E = Elem<DT>;
     using raw = typename E::raw;
@@ -205,10 +299,11 @@ __device__ __forceinline__ void store_rows(const ApplyArgs &a, int p0, int rows_
     for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int key = __shfl(f.key[tb], kq * 4 + i, 64);
+            const int tok = __shfl(f.tok[tb], kq * 4 + i, 64);
             const int p = p0 + tb * 16 + kq * 4 + i;
             if (p >= rows_end) continue;
-            const int key = a.rv.segs[4 * a.rv.pos_seg[p]];
-            const size_t base = static_cast<size_t>(token_of(a, p)) * a.d_out + n0 + r;
+            const size_t base = static_cast<size_t>(tok) * a.d_out + n0 + r;
 #pragma unroll
             for (int wc = 0; wc < WC; ++wc)
                 y[base + wc * 16] = (key == a.S + 1) ? E::qnan : E::from_f(acc[tb][wc][i]);

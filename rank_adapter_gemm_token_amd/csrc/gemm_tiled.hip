@@ -122,8 +122,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
 
     const int pw = m0 + wm * TB * 16;
     const int nw = n0 + wn * WC * 16;
-    lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, acc);
-    store_rows<DT, TB, WC>(a, pw, a.T, nw, acc);
+    RowFacts<TB> f;
+    row_facts<TB>(a, pw, a.T, f);
+    lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, f, acc);
+    store_rows<DT, TB, WC>(a, pw, a.T, nw, f, acc);
 }
 
 // 256-row tiles, operands straight into LDS.  A workgroup of 8 waves (2 x
@@ -271,8 +273,10 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     asm volatile("" : "+s"(pw));
     const int nw = n0 + wn * WC * 16;
     if (!SPLIT) {
-        lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, acc);
-        store_rows<DT, TB, WC>(a, pw, a.T, nw, acc);
+        RowFacts<TB> f;
+        row_facts<TB>(a, pw, a.T, f);
+        lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, f, acc);
+        store_rows<DT, TB, WC>(a, pw, a.T, nw, f, acc);
     } else {
         // Partial sums [z][16-row block][16-column block][lane], row blocks
         // of sorted rows below T only.
@@ -318,8 +322,10 @@ __global__ __launch_bounds__(256) void k_split_epilogue(ApplyArgs a, const float
         for (int z = 1; z < MAX_TSPLIT; ++z)
             if (z < splits) acc[0][wc] += v[z][wc];
     }
-    lora_expand_mfma<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, SEG_FUSED, acc);
-    store_rows<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, acc);
+    RowFacts<1> f;
+    row_facts<1>(a, rb * 16, a.T, f);
+    lora_expand_mfma<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, SEG_FUSED, f, acc);
+    store_rows<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, f, acc);
 }
 
 template <int DT, int BM, int BN>

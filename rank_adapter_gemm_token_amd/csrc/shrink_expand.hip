@@ -44,13 +44,16 @@ __global__ __launch_bounds__(256) void k_expand_sep(ApplyArgs a) {
     const int kq = lane >> 4;
     const int n0 = blockIdx.y * 64 + wave * 16;
     f32x4_t acc[1][1] = {{f32x4_t{0.f, 0.f, 0.f, 0.f}}};
-    lora_expand_mfma<DT, 1, 1>(a, row0, rows_end, n0, SEG_SEPARATE, acc);
+    RowFacts<1> f;
+    row_facts<1>(a, row0, rows_end, f);
+    lora_expand_mfma<DT, 1, 1>(a, row0, rows_end, n0, SEG_SEPARATE, f, acc);
     raw *y = static_cast<raw *>(a.y);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        const int tok = __shfl(f.tok[0], kq * 4 + i, 64);
         const int p = row0 + kq * 4 + i;
         if (p >= rows_end) continue;
-        raw *yp = y + static_cast<size_t>(token_of(a, p)) * a.d_out + n0 + r;
+        raw *yp = y + static_cast<size_t>(tok) * a.d_out + n0 + r;
         *yp = E::from_f(E::to_f(*yp) + acc[0][0][i]);
     }
 }
