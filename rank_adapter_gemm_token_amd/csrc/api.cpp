@@ -240,7 +240,12 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     // per k split of their GEMM, [splits][T][Rp], and the splits' partial
     // sums [splits][T rounded up to 16 .. 64][d_out].
     const int dec_splits = (esz == 2) ? lora::decode_splits(static_cast<int>(dec_T), d_in) : 0;
-    const size_t h_rows = std::max(T, static_cast<size_t>(dec_splits) * dec_T);
+    // Calls on the tiled path keep tiled_h_parts parts, [parts][T][Rp].
+    size_t h_rows = std::max(T, static_cast<size_t>(dec_splits) * dec_T);
+    if (esz == 2)
+        for (int t = 1; t <= max_tokens; ++t)
+            h_rows = std::max(h_rows, static_cast<size_t>(t) *
+                                          lora::tiled_h_parts(d_in, Rp, lora::max_tiles(t, n_slots)));
     const size_t o_h = take(h_rows * Rp * 4);
     const size_t dec_rows = static_cast<size_t>(lora::decode_token_blocks(static_cast<int>(dec_T))) * 16;
     // Split-K partial sums of calls of 65 .. 2047 tokens: the largest
@@ -434,6 +439,7 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
         HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
                                    p->ro, st));
         HIP_TRY(mark(1));
+        if (half) a.h_parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound);
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
         if (half) {

@@ -121,16 +121,33 @@ __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int pa
 }
 
 // h[p][j .. j+7] summed over the shrink's k parts in order (p: the h row,
-// a sorted position or a token).
+// a sorted position or a token).  The first HP parts' loads are all in flight
+// before the first add; parts beyond HP (if any) are added one at a time.
+template <int HP>
 __device__ __forceinline__ void load_h8(const ApplyArgs &a, int p, int j, float (&hv)[8]) {
     const size_t stride = static_cast<size_t>(a.T) * a.R;
-    const float4 *hp = reinterpret_cast<const float4 *>(a.h + static_cast<size_t>(p) * a.R + j);
-    float4 h0 = hp[0], h1 = hp[1];
-    for (int q = 1; q < a.h_parts; ++q) {
-        const float4 *hq = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(hp) + q * stride);
-        const float4 g0 = hq[0], g1 = hq[1];
-        h0.x += g0.x; h0.y += g0.y; h0.z += g0.z; h0.w += g0.w;
-        h1.x += g1.x; h1.y += g1.y; h1.z += g1.z; h1.w += g1.w;
+    const float *hp = a.h + static_cast<size_t>(p) * a.R + j;
+    const int np = uniform(a.h_parts);
+    float4 v[HP][2];
+#pragma unroll
+    for (int q = 0; q < HP; ++q) {
+        if (q < np) {
+            const float4 *hq = reinterpret_cast<const float4 *>(hp + q * stride);
+            v[q][0] = hq[0];
+            v[q][1] = hq[1];
+        }
+    }
+    float4 h0 = v[0][0], h1 = v[0][1];
+    auto add = [&](const float4 &u0, const float4 &u1) {
+        h0.x += u0.x; h0.y += u0.y; h0.z += u0.z; h0.w += u0.w;
+        h1.x += u1.x; h1.y += u1.y; h1.z += u1.z; h1.w += u1.w;
+    };
+#pragma unroll
+    for (int q = 1; q < HP; ++q)
+        if (q < np) add(v[q][0], v[q][1]);
+    for (int q = HP; q < np; ++q) {
+        const float4 *hq = reinterpret_cast<const float4 *>(hp + q * stride);
+        add(hq[0], hq[1]);
     }
     hv[0] = h0.x; hv[1] = h0.y; hv[2] = h0.z; hv[3] = h0.w;
     hv[4] = h1.x; hv[5] = h1.y; hv[6] = h1.z; hv[7] = h1.w;
@@ -182,7 +199,7 @@ __device__ __forceinline__ void row_facts(const ApplyArgs &a, int p0, int rows_e
 // usual case for long buckets) its B fragments are loaded once; otherwise
 // each block meets its buckets one at a time (rows are sorted, so a bucket
 // is a run of lanes), one round of B loads per bucket.
-template <int DT, int TB, int WC>
+template <int DT, int TB, int WC, int HP = MAX_HPARTS>
 __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int rows_end, int n0, int want,
                                                  const RowFacts<TB> &f, f32x4_t (&acc)[TB][WC]) {
     using E = Elem<DT>;
@@ -206,7 +223,7 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
     // clamped row and rank).
     auto load_h = [&](int tb, int js, float (&hv)[8]) {
         const int hrow = a.h_by_token ? f.tok[tb] : min(p0 + tb * 16 + r, rows_end - 1);
-        load_h8(a, hrow, min(js * 32 + 8 * kq, Rp - 8), hv);
+        load_h8<HP>(a, hrow, min(js * 32 + 8 * kq, Rp - 8), hv);
     };
     // H operand of block tb, rank step js, for bucket gg (-1: any bucket of
     // mode `want`).

@@ -275,7 +275,8 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     if (!SPLIT) {
         RowFacts<TB> f;
         row_facts<TB>(a, pw, a.T, f);
-        lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, f, acc);
+        // Calls this large take one shrink part (tiled_h_parts).
+        lora_expand_mfma<DT, TB, WC, 1>(a, pw, a.T, nw, SEG_FUSED, f, acc);
         store_rows<DT, TB, WC>(a, pw, a.T, nw, f, acc);
     } else {
         // Partial sums [z][16-row block][16-column block][lane], row blocks

@@ -101,6 +101,10 @@ struct ApplyArgs {
 
 hipError_t launch_shrink(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_shrink16(const ApplyArgs &a, hipStream_t st);
+// k parts of the fp16/bf16 shrink on the tiled path (h_parts) for a call of
+// at most `tiles` bucket tiles; consumers add the parts in order.
+constexpr int MAX_HPARTS = 8;
+int tiled_h_parts(int d_in, int R, int tiles);
 hipError_t launch_expand_sep16(const ApplyArgs &a, hipStream_t st);
 // Optional timing events of one launch: when `start` is set, the kernel is
 // launched with hipExtLaunchKernelGGL, which records both events from the

@@ -24,6 +24,8 @@ namespace {
 
 constexpr int RT = 1024;
 constexpr int RW = RT / 64;
+constexpr int KEY_CAP = 32768;   // tokens whose keys stay in LDS (2 bytes each)
+constexpr int IDX_UNROLL = 4;    // index loads per thread in flight
 
 __device__ __forceinline__ int key_of(int32_t v, int S, const SlotDev *__restrict__ slots) {
     if (v == -1) return S;
@@ -42,6 +44,8 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     __shared__ unsigned short s_wc[RW][MAX_KEYS];
     __shared__ int s_tot[4];  // buckets, tiles, fused buckets, separate buckets
     __shared__ int s_rows[2]; // padded rows, true rows
+    __shared__ unsigned char s_act[MAX_KEYS];     // slot k is ACTIVE
+    __shared__ unsigned short s_key[KEY_CAP];     // token -> key (T <= KEY_CAP)
 
     const int K = S + 2;
     const int tid = threadIdx.x;
@@ -57,8 +61,25 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     if (tid < 2) s_rows[tid] = 0;
     __syncthreads();
 
-    // Histogram (integer LDS atomics: the counts do not depend on order).
-    for (int t = tid; t < T; t += RT) atomicAdd(&s_cnt[key_of(idx[t], S, slots)], 1);
+    // Keys.  Every slot's state goes to LDS and every index is read once
+    // (IDX_UNROLL per thread in flight); a token's key is then an LDS
+    // lookup, kept in LDS for the scatter when T <= KEY_CAP.
+    const bool keep = T <= KEY_CAP;
+    for (int k = tid; k < S; k += RT) s_act[k] = slots[k].state == SLOT_ACTIVE;
+    __syncthreads();
+    for (int t0 = 0; t0 < T; t0 += RT * IDX_UNROLL) {
+        int v[IDX_UNROLL];
+#pragma unroll
+        for (int u = 0; u < IDX_UNROLL; ++u) v[u] = idx[min(t0 + u * RT + tid, T - 1)];
+#pragma unroll
+        for (int u = 0; u < IDX_UNROLL; ++u) {
+            const int t = t0 + u * RT + tid;
+            if (t >= T) continue;
+            const int key = (v[u] == -1) ? S : ((v[u] >= 0 && v[u] < S && s_act[v[u]]) ? v[u] : S + 1);
+            if (keep) s_key[t] = static_cast<unsigned short>(key);
+            atomicAdd(&s_cnt[key], 1);  // integer LDS atomics: counts do not depend on order
+        }
+    }
     __syncthreads();
 
     // Exclusive scans over keys of: counts, non-empty flags, LoRA tiles.
@@ -137,7 +158,7 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     for (int c0 = 0; c0 < T; c0 += RT) {
         const int t = c0 + tid;
         const bool v = t < T;
-        const int key = v ? key_of(idx[t], S, slots) : K;
+        const int key = !v ? K : (keep ? static_cast<int>(s_key[t]) : key_of(idx[t], S, slots));
         unsigned long long peers = ~0ull;
         for (int b = 0; b < nbits; ++b) {
             const int bit = (key >> b) & 1;

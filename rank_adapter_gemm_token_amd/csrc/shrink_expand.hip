@@ -15,6 +15,8 @@
 //
 // Separate expand: one workgroup of 4 waves per (tile of a SEPARATE bucket,
 // 64 columns); acc = s * h . B on MFMA, then y = round(y + acc).
+#include <algorithm>
+
 #include "epilogue.hpp"
 
 namespace lora {
@@ -24,7 +26,8 @@ namespace {
 template <int DT, int RB>
 __global__ __launch_bounds__(256) void k_shrink(ApplyArgs a) {
     __shared__ u32x4_t lds[4 * RB * 64];
-    shrink_role<DT, RB, 4>(a, blockIdx.x, 0, lds);
+    // Unit (tile, k part): part-major within a tile.
+    shrink_role<DT, RB, 4>(a, blockIdx.x / a.h_parts, blockIdx.x % a.h_parts, lds);
 }
 
 template <int DT>
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void k_expand_sep(ApplyArgs a) {
 
 template <int DT>
 hipError_t shrink_rb(const ApplyArgs &a, hipStream_t st) {
-    const dim3 grid(a.tiles_bound);
+    const dim3 grid(a.tiles_bound * a.h_parts);
     switch ((a.R + 15) / 16) {
         case 1: hipLaunchKernelGGL((k_shrink<DT, 1>), grid, dim3(256), 0, st, a); break;
         case 2: hipLaunchKernelGGL((k_shrink<DT, 2>), grid, dim3(256), 0, st, a); break;
@@ -74,6 +77,21 @@ hipError_t shrink_rb(const ApplyArgs &a, hipStream_t st) {
 
 hipError_t launch_shrink16(const ApplyArgs &a, hipStream_t st) {
     return (a.dtype == DT_F16) ? shrink_rb<DT_F16>(a, st) : shrink_rb<DT_BF16>(a, st);
+}
+
+int tiled_h_parts(int d_in, int R, int tiles) {
+    // With few tiles (a few workgroups per CU at most) each wave's chain of
+    // dependent load rounds sets the time: split k until each wave has about
+    // one round (U k steps as in shrink_unit: 16, 8 or 4 for 1, 2, 3-4 rank
+    // blocks) or the grid reaches ~512 workgroups.  With many tiles the
+    // chip is full already and extra parts only add h traffic.
+    if (tiles >= 256) return 1;
+    const int rb = (R + 15) / 16;
+    const int u = rb == 1 ? 16 : rb == 2 ? 8 : 4;
+    const int kst = d_in / 32;
+    int p = (kst + 4 * u - 1) / (4 * u);
+    p = std::min(p, (512 + tiles - 1) / tiles);
+    return std::max(1, std::min(p, MAX_HPARTS));
 }
 
 hipError_t launch_expand_sep16(const ApplyArgs &a, hipStream_t st) {
