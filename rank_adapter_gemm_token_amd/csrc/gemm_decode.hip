@@ -54,8 +54,6 @@ constexpr int DCB = 4;               // 16-column blocks per GEMM workgroup
 constexpr int DCOLS = DCB * 16;      // columns per GEMM workgroup
 constexpr int DSTEPS_PER_WAVE = 8;   // k steps a GEMM wave holds at once
 constexpr int SMAX_SEG = DECODE_MAX_T + 2;
-constexpr int SLOT_CAP = MAX_KEYS - 2;
-constexpr int SLOT_LD = SLOT_CAP / (NWK * 64);  // slot-table loads per thread
 
 // ------------------------------------------------------ small-call routing --
 
@@ -79,45 +77,50 @@ struct SmallRoute {
     int stat[6];                // fused, separate, base_only, invalid, rows padded, rows true
 };
 
-// Wave 0: key = slot (active), S (base_only) or S + 1 (invalid) of each
-// token, then each token's sorted position = #(smaller keys) + #(same key,
-// smaller index); buckets, modes, tiles and statistics from ballots.
-// `slot_sr` holds {state, rank} of every slot (LDS).  Other waves return.
-__device__ __forceinline__ void small_route(int v, int T, int S, const int2 *slot_sr, int max_rank, int policy, int theta,
-                            SmallRoute &sr) {
+// One wave: key = slot (active), S (base_only) or S + 1 (invalid) of the
+// token of each lane (lanes >= T: S + 2, after every token), then each
+// token's sorted position = #(smaller keys) + #(same key, smaller index),
+// counted from one ballot per key bit; buckets, modes, tiles and statistics
+// from ballots.  `v` is the lane's adapter index and `state`, `rank` the
+// entry of slot v (any values when v is not a slot).
+__device__ __forceinline__ void small_route(int v, int state, int rank_in, int T, int S, int max_rank, int policy,
+                                            int theta, SmallRoute &sr) {
     const int lane = threadIdx.x & 63;
-    if (threadIdx.x >= 64) return;
     const bool tv = lane < T;
     int key = S, rank = 0;
     if (v != -1) {
         key = S + 1;
-        if (v >= 0 && v < S) {
-            const int2 e = slot_sr[v];
-            if (e.x == SLOT_ACTIVE) {
-                key = v;
-                rank = e.y;
-            }
+        if (v >= 0 && v < S && state == SLOT_ACTIVE) {
+            key = v;
+            rank = rank_in;
         }
     }
-    if (!tv) key = 0x7FFF;
+    if (!tv) key = S + 2;
     sr.key[lane] = key;
     sr.rank[lane] = rank;
-    lds_fence();
+    // Rank by key, most significant bit first: `eq` holds the lanes whose
+    // key agrees with this lane's on the bits seen so far.
+    const int nbits = 32 - __clz(S + 2);
+    unsigned long long eq = ~0ull;
     int pos = 0;
-#pragma unroll
-    for (int j4 = 0; j4 < DECODE_MAX_T; j4 += 4) {
-        const int4 k4 = *reinterpret_cast<const int4 *>(&sr.key[j4]);
-        const int kk[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) pos += (kk[u] < key || (kk[u] == key && j4 + u < lane)) ? 1 : 0;
+    for (int b = nbits - 1; b >= 0; --b) {
+        const unsigned long long m = __ballot((key >> b) & 1);
+        if ((key >> b) & 1) {
+            pos += __popcll(eq & ~m);
+            eq &= m;
+        } else {
+            eq &= ~m;
+        }
     }
+    pos += __popcll(eq & ((1ull << lane) - 1ull));
+    lds_fence();
     if (tv) sr.perm[pos] = lane;
     lds_fence();
     // Lane p: the token at sorted position p.
     const int p = lane;
     const bool pv = p < T;
     const int ptok = pv ? sr.perm[p] : 0;
-    const int pkey = pv ? sr.key[ptok] : 0x7FFF;
+    const int pkey = pv ? sr.key[ptok] : S + 2;
     const int prev = (p > 0 && pv) ? sr.key[sr.perm[p - 1]] : -1;
     const bool start = pv && prev != pkey;
     const unsigned long long starts = __ballot(start);
@@ -181,19 +184,19 @@ __device__ __forceinline__ void small_route(int v, int T, int S, const int2 *slo
     }
 }
 
-// Workgroup 0: publish the routing for the epilogue and residual kernels, the
-// statistics and the invalid-token count.
+// The routing wave of workgroup 0: publish the routing for the residual
+// kernel and the caller, the statistics and the invalid-token count.
 __device__ __forceinline__ void publish_route(const SmallRoute &sr, int T, const RouteOut &out) {
-    const int tid = threadIdx.x;
-    for (int i = tid; i < T; i += blockDim.x) {
-        out.perm[i] = sr.perm[i];
-        out.pos_seg[i] = sr.pos_seg[i];
-        out.tok_pos[i] = sr.tok_pos[i];
-        out.tok_seg[i] = sr.tok_seg[i];
+    const int lane = threadIdx.x & 63;
+    if (lane < T) {
+        out.perm[lane] = sr.perm[lane];
+        out.pos_seg[lane] = sr.pos_seg[lane];
+        out.tok_pos[lane] = sr.tok_pos[lane];
+        out.tok_seg[lane] = sr.tok_seg[lane];
     }
-    for (int i = tid; i < 4 * sr.n_seg; i += blockDim.x) out.segs[i] = sr.segs[i >> 2][i & 3];
-    for (int i = tid; i < 2 * sr.n_tiles; i += blockDim.x) out.tiles[i] = sr.tiles[i >> 1][i & 1];
-    if (tid == 0) {
+    for (int i = lane; i < 4 * sr.n_seg; i += 64) out.segs[i] = sr.segs[i >> 2][i & 3];
+    for (int i = lane; i < 2 * sr.n_tiles; i += 64) out.tiles[i] = sr.tiles[i >> 1][i & 1];
+    if (lane == 0) {
         *out.n_seg = sr.n_seg;
         *out.n_tiles = sr.n_tiles;
         DevStats st;
@@ -360,18 +363,19 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 // -------------------------------------------------------------- epilogue --
 
-// Workgroup: 4 waves, one 16-column block; thread (tb = wave < TB, lane)
-// holds rows tb*16 + 4*(lane/16) + i of column lane % 16.
+// Workgroup: NWK waves for one 16-column block, thread (tb = wave < TB,
+// lane) holding rows tb*16 + 4*(lane/16) + i of column lane % 16, plus one
+// routing wave.  The routing wave loads only the token indices and their slot
+// entries, so its waits never include the row waves' loads.
 template <int DT, int TB, int RB>
-__global__ __launch_bounds__(NWK * 64) void k_decode_epilogue(ApplyArgs a, DecodeArgs d, const int32_t *__restrict__ idx,
-                                                              RouteOut out) {
+__global__ __launch_bounds__((NWK + 1) * 64) void k_decode_epilogue(ApplyArgs a, DecodeArgs d,
+                                                                    const int32_t *__restrict__ idx, RouteOut out) {
     using E = Elem<DT>;
     using raw = typename E::raw;
     constexpr int HR = RB * 16;
     constexpr int TP = TB * 16;
-    constexpr int HQ = (TP * HR / 4 + NWK * 64 - 1) / (NWK * 64);  // h float4s per thread
+    constexpr int HQ = (TP * HR / 4 + NWK * 64 - 1) / (NWK * 64);  // h float4s per row-wave thread
     __shared__ float hs[TP][HR + 1];
-    __shared__ int2 s_slot[SLOT_CAP];
     __shared__ SmallRoute sr;
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6);
@@ -381,85 +385,100 @@ __global__ __launch_bounds__(NWK * 64) void k_decode_epilogue(ApplyArgs a, Decod
     const int nb = blockIdx.x;  // 16-column block
     const int n = nb * 16 + (lane & 15);
 
-    // Round 1, all independent: routing inputs, the splits' partial sums,
-    // the h parts.
-    const int v_idx = idx[min(lane, T - 1)];
-    int2 sl[SLOT_LD];
-#pragma unroll
-    for (int u = 0; u < SLOT_LD; ++u)
-        sl[u] = reinterpret_cast<const int2 *>(a.slots)[2 * min(tid + u * NWK * 64, a.S - 1)];
+    if (wave == NWK) {
+        // Routing wave: token index, then its slot entry; the routing in LDS,
+        // published by workgroup 0.
+        const int v = lane < T ? idx[min(lane, T - 1)] : -1;
+        const int2 e = reinterpret_cast<const int2 *>(a.slots)[2 * min(max(v, 0), a.S - 1)];
+        small_route(v, e.x, e.y, T, a.S, d.max_rank, a.policy, d.theta, sr);
+        if (blockIdx.x == 0) publish_route(sr, T, out);
+        __syncthreads();
+        return;
+    }
+
+    // Row waves: the adapter index of this thread's 4 rows, then, as soon as
+    // they arrive, the B rows and scales of their slots (clamped: used only
+    // for FUSED rows, whose key is that index); then the splits' partial sums
+    // and the h parts.
     const int tb = min(wave, TB - 1);
+    int vi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vi[i] = idx[min(tb * 16 + (lane >> 4) * 4 + i, T - 1)];
+    u32x4_t bw[4][2 * RB];
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int kc = min(max(vi[i], 0), a.S - 1);
+        const uint16_t *bp = static_cast<const uint16_t *>(a.B_slab) + (static_cast<size_t>(kc) * a.d_out + n) * Rp;
+#pragma unroll
+        for (int qb = 0; qb < 2 * RB; ++qb) bw[i][qb] = *reinterpret_cast<const u32x4_t *>(bp + min(8 * qb, Rp - 8));
+        sc[i] = a.slots[kc].scale;
+    }
+    // Splits are taken SQ at a time (all of them at once for d_in <= 4096),
+    // each group's loads in flight together, and added in split order.
+    constexpr int SQ = 4;
     const f32x4_t *part = reinterpret_cast<const f32x4_t *>(d.part) + (static_cast<size_t>(nb) * TB + tb) * 64 + lane;
     const size_t qstride = static_cast<size_t>(a.d_out / 16) * TB * 64;
-    f32x4_t pv[MAX_DSPLIT];
-#pragma unroll
-    for (int qq = 0; qq < MAX_DSPLIT; ++qq)
-        if (qq < d.splits) pv[qq] = part[qq * qstride];
     const int hq_n = T * Rp / 4;
     const size_t pstride = static_cast<size_t>(T) * Rp / 4;
-    float4 hv[HQ][MAX_DSPLIT];
+    const float4 *hp = reinterpret_cast<const float4 *>(a.h);
+    f32x4_t acc;
+    float4 hsum[HQ];
+    for (int q0 = 0; q0 < d.splits; q0 += SQ) {
+        f32x4_t pv[SQ];
+        float4 hv[HQ][SQ];
 #pragma unroll
-    for (int m = 0; m < HQ; ++m)
+        for (int u = 0; u < SQ; ++u)
+            if (q0 + u < d.splits) pv[u] = part[(q0 + u) * qstride];
 #pragma unroll
-        for (int qq = 0; qq < MAX_DSPLIT; ++qq)
-            if (qq < d.splits)
-                hv[m][qq] = reinterpret_cast<const float4 *>(a.h)[qq * pstride + min(tid + m * NWK * 64, hq_n - 1)];
-
-    // Routing in LDS (wave 0), published by workgroup 0.
+        for (int m = 0; m < HQ; ++m)
 #pragma unroll
-    for (int u = 0; u < SLOT_LD; ++u)
-        if (tid + u * NWK * 64 < a.S) s_slot[tid + u * NWK * 64] = sl[u];
-    __syncthreads();
-    small_route(lane < T ? v_idx : -1, T, a.S, s_slot, d.max_rank, a.policy, d.theta, sr);
-    // h (parts summed in order), by token.
+            for (int u = 0; u < SQ; ++u)
+                if (q0 + u < d.splits) hv[m][u] = hp[(q0 + u) * pstride + min(tid + m * NWK * 64, hq_n - 1)];
+        if (q0 == 0) {
+            acc = pv[0];
+#pragma unroll
+            for (int m = 0; m < HQ; ++m) hsum[m] = hv[m][0];
+        }
+#pragma unroll
+        for (int u = 0; u < SQ; ++u) {
+            if ((q0 > 0 || u > 0) && q0 + u < d.splits) {
+                acc += pv[u];
+#pragma unroll
+                for (int m = 0; m < HQ; ++m) {
+                    hsum[m].x += hv[m][u].x;
+                    hsum[m].y += hv[m][u].y;
+                    hsum[m].z += hv[m][u].z;
+                    hsum[m].w += hv[m][u].w;
+                }
+            }
+        }
+    }
+    // h by token, to LDS.
 #pragma unroll
     for (int m = 0; m < HQ; ++m) {
         const int e = tid + m * NWK * 64;
         if (e < hq_n) {
-            float4 v = hv[m][0];
-#pragma unroll
-            for (int qq = 1; qq < MAX_DSPLIT; ++qq) {
-                if (qq < d.splits) {
-                    v.x += hv[m][qq].x;
-                    v.y += hv[m][qq].y;
-                    v.z += hv[m][qq].z;
-                    v.w += hv[m][qq].w;
-                }
-            }
             const int t = (e * 4) / Rp, j = (e * 4) % Rp;
-            hs[t][j] = v.x;
-            hs[t][j + 1] = v.y;
-            hs[t][j + 2] = v.z;
-            hs[t][j + 3] = v.w;
+            hs[t][j] = hsum[m].x;
+            hs[t][j + 1] = hsum[m].y;
+            hs[t][j + 2] = hsum[m].z;
+            hs[t][j + 3] = hsum[m].w;
         }
     }
     __syncthreads();
-    if (blockIdx.x == 0) publish_route(sr, T, out);
     if (wave >= TB) return;
 
-    f32x4_t acc = pv[0];
-#pragma unroll
-    for (int qq = 1; qq < MAX_DSPLIT; ++qq)
-        if (qq < d.splits) acc += pv[qq];
-    // Round 2, FUSED rows: B rows of their slots and the scales.
+    // FUSED rows: the key of a LoRA token is its adapter index, so the B
+    // rows loaded above are its slot's.
     int key[4];
     bool fused[4];
-    u32x4_t bw[4][2 * RB];
-    float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = tb * 16 + (lane >> 4) * 4 + i;
         const int sg = sr.tok_seg[min(t, T - 1)];
         key[i] = sr.segs[sg][0];
         fused[i] = t < T && key[i] < a.S && sr.segs[sg][3] == SEG_FUSED;
-        sc[i] = 0.0f;
-        if (fused[i]) {
-            const uint16_t *bp =
-                static_cast<const uint16_t *>(a.B_slab) + (static_cast<size_t>(key[i]) * a.d_out + n) * Rp;
-#pragma unroll
-            for (int qb = 0; qb < 2 * RB; ++qb) bw[i][qb] = *reinterpret_cast<const u32x4_t *>(bp + min(8 * qb, Rp - 8));
-            sc[i] = a.slots[key[i]].scale;
-        }
     }
     raw *y = static_cast<raw *>(a.y);
 #pragma unroll
@@ -492,6 +511,7 @@ hipError_t launch_tb(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx
     const dim3 grid((a.d_out / DCOLS) * d.splits);
     const dim3 egrid(a.d_out / 16);
     const dim3 block(NWK * 64);
+    const dim3 eblock((NWK + 1) * 64);
     switch ((a.R + 15) / 16) {
         case 1: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 1>), grid, block, 0, st, a, d, idx); break;
         case 2: LORA_LAUNCH(ev, (k_decode_gemm<DT, TB, 2>), grid, block, 0, st, a, d, idx); break;
@@ -501,10 +521,10 @@ hipError_t launch_tb(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch ((a.R + 15) / 16) {
-        case 1: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 1>), egrid, block, 0, st, a, d, idx, out); break;
-        case 2: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 2>), egrid, block, 0, st, a, d, idx, out); break;
-        case 3: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 3>), egrid, block, 0, st, a, d, idx, out); break;
-        default: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 4>), egrid, block, 0, st, a, d, idx, out); break;
+        case 1: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 1>), egrid, eblock, 0, st, a, d, idx, out); break;
+        case 2: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 2>), egrid, eblock, 0, st, a, d, idx, out); break;
+        case 3: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 3>), egrid, eblock, 0, st, a, d, idx, out); break;
+        default: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 4>), egrid, eblock, 0, st, a, d, idx, out); break;
     }
     return hipGetLastError();
 }
