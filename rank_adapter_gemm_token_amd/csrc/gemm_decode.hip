@@ -12,21 +12,23 @@
 // kernel waits for routing:
 //
 // k_decode_gemm -- workgroup (column group c of 64 columns, k split q), 4
-//   waves (one per SIMD, 512 registers each); wave w holds the split's k
-//   steps w, w+4, ..., w+28 for all 64 columns and all T rows.
-//   * Loads are issued all at once, through buffer resources (uniform
-//     column-block and step offsets): the adapter index of every token, the
-//     A rows of slot c for the split's steps (requested before the token
-//     indices are known -- they are few), then every x and W fragment of the
-//     wave, so the whole of the workgroup's W tile is in flight from the
-//     start.
-//   * GEMM: fp32 MFMA accumulators over the wave's steps; the 4 waves' sums
+//   waves (one per SIMD, 512 registers each); wave w takes the split's k
+//   step pairs p = w, w+4, w+8, w+12 (64 k each) for all 64 columns and all
+//   T rows.
+//   * Operands go from global memory straight into LDS (buffer_load ... lds),
+//     one instruction per 8 rows with 8 lanes covering each row's 128-byte
+//     line, into a per-wave ring of 2-3 pair slots (128 KiB in all); the
+//     MFMA operands are read back from XOR-swizzled rows without bank
+//     conflicts.  Each wave waits only for its own loads (no barrier in the
+//     loop).  The A rows of slot c are requested first, into registers
+//     (before the token indices are known -- a slot is named by few tokens
+//     if any).
+//   * GEMM: fp32 MFMA accumulators over the wave's pairs; the 4 waves' sums
 //     are added in LDS in a fixed order and stored as the split's partial
 //     sums in MFMA fragment order (16 bytes a lane, coalesced).
-//   * Shrink: for slots c, c + groups, ... that some token names and that
-//     are active, this split's part of h = x . A_slot^T for all T rows from
-//     the x fragments already held, rows of that slot's tokens kept (fp32,
-//     by token, part q).
+//   * Shrink: in the same loop, this split's part of h = x . A_c^T for all T
+//     rows, rows of slot c's tokens kept (fp32, by token, part q); slots c +
+//     groups, ... (pools with more slots than column groups) read x again.
 // k_decode_epilogue -- one 16-column block per workgroup, thread (row block,
 //   lane) = 4 rows of one column.  The splits' partial sums and the h parts
 //   are requested first; meanwhile wave 0 routes the (at most 64) tokens in
@@ -52,7 +54,7 @@ namespace {
 constexpr int NWK = 4;               // waves per workgroup (one per SIMD)
 constexpr int DCB = 4;               // 16-column blocks per GEMM workgroup
 constexpr int DCOLS = DCB * 16;      // columns per GEMM workgroup
-constexpr int DSTEPS_PER_WAVE = 8;   // k steps a GEMM wave holds at once
+constexpr int DPAIRS_PER_WAVE = 4;   // k step pairs per GEMM wave
 constexpr int SMAX_SEG = DECODE_MAX_T + 2;
 
 // ------------------------------------------------------ small-call routing --
@@ -215,14 +217,56 @@ __device__ __forceinline__ void publish_route(const SmallRoute &sr, int T, const
 
 // ------------------------------------------------------------------ GEMM --
 
+using lds_ptr = __attribute__((address_space(3))) void *;
+
+// Waits until at most N vector-memory operations of this wave are
+// outstanding (they complete in order), and keeps the compiler from moving
+// memory accesses across the wait.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One step pair into a ring slot: nx x-row instructions then W-row ones up
+// to nl, instruction g filling the slot's 16-byte units 64 g .. 64 g + 63.
+__device__ __forceinline__ void issue_pair(const __amdgpu_buffer_rsrc_t &xrs, const __amdgpu_buffer_rsrc_t &wrs,
+                                           u32x4_t *slot, const uint32_t *loff, int nx, int nl, uint32_t soff) {
+#pragma unroll
+    for (int g = 0; g < nx; ++g)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(slot + g * 64), 16, loff[g], soff, 0, 0);
+#pragma unroll
+    for (int g = nx; g < nl; ++g)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(slot + g * 64), 16, loff[g], soff, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Ring slots per wave for TB token blocks: a slot holds one step pair of x
+// (16 TB rows) and W (64 rows), 128 bytes a row; the ring of the 4 waves
+// stays within 128 KiB.
+template <int TB>
+struct DecRing {
+    static constexpr int XROWS = TB * 16;
+    static constexpr int UNITS = (XROWS + DCOLS) * 8;          // 16-byte units per slot
+    static constexpr int LOADS = (XROWS + DCOLS) / 8;          // load instructions per slot
+    static constexpr int FIT = (128 * 1024 / 16) / (NWK * UNITS);
+    static constexpr int SLOTS = FIT < DPAIRS_PER_WAVE ? FIT : DPAIRS_PER_WAVE;
+};
+
 template <int DT, int TB, int RB>
 __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_decode_gemm(
     ApplyArgs a, DecodeArgs d, const int32_t *__restrict__ idx) {
     using E = Elem<DT>;
     using V = typename E::vec8;
+    using Ring = DecRing<TB>;
     constexpr int NB = TB * DCB;  // 16x16 output blocks per wave
-    constexpr int GS = DSTEPS_PER_WAVE;
-    __shared__ f32x4_t red[NWK * NB * 64];  // cross-wave sums (64 KiB at TB = 4)
+    constexpr int PPW = DPAIRS_PER_WAVE;
+    constexpr int RS = Ring::SLOTS;
+    constexpr int L = Ring::LOADS;
+    static_assert(RS >= 1, "ring");
+    static_assert(NWK * NB * 64 <= NWK * RS * Ring::UNITS, "cross-wave sums fit in the ring");
+    // Per-wave rings of step pairs; after the main loop, the cross-wave sums.
+    __shared__ u32x4_t smem[NWK * RS * Ring::UNITS];
 
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6);
@@ -236,70 +280,125 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int q = uniform(blockIdx.x / ncg);
     const int c0 = cg * DCOLS;
     const int kst = a.d_in >> 5;
-    const int qa = q * kst / d.splits;
-    const int nsq = (q + 1) * kst / d.splits - qa;  // k steps of this split (>= 1)
-
-    // Buffer loads: one per-lane byte offset per operand row; column blocks,
-    // the wave's steps and the per-step stride are uniform (SGPR or
-    // immediate offsets), so addressing costs few registers.
+    const int kp = kst >> 1;  // step pairs (d_in % 64 == 0)
+    const int pa = uniform(q * kp / d.splits);
+    const int pn = uniform((q + 1) * kp / d.splits - pa);  // pairs of this split (1 .. NWK * PPW)
     const uint32_t rowb = static_cast<uint32_t>(a.d_in) * 2;  // bytes per row
-    const uint32_t kb = static_cast<uint32_t>(qa) * 64 + 16 * kq;
-    auto step_b = [&](int i) { return static_cast<uint32_t>(min(wave + NWK * i, nsq - 1)) * 64; };
+    // Pair i of this wave: split pair wave + NWK i (valid when < pn); its two
+    // k steps are 2 (pa + p) and 2 (pa + p) + 1.
+    auto pair_of = [&](int i) { return wave + NWK * i; };
 
-    // 1. Adapter index of token `lane` (every wave holds all T of them), and
-    //    the A fragments of slot cg for this wave's steps.
-    const int my_idx = idx[min(lane, T - 1)];
-    V af[GS][RB];
-    auto load_a = [&](int s) {
+    // 1. The A fragments of slot cg for this wave's steps (requested before
+    //    the token indices are known: a slot is named by few tokens if any).
+    V af[PPW][2][RB];
+    const bool shrink0 = cg < a.S;
+    if (shrink0) {
         const __amdgpu_buffer_rsrc_t ars =
-            make_rsrc(static_cast<const uint16_t *>(a.A_slab) + static_cast<size_t>(s) * Rp * a.d_in, Rp * rowb);
+            make_rsrc(static_cast<const uint16_t *>(a.A_slab) + static_cast<size_t>(cg) * Rp * a.d_in, Rp * rowb);
 #pragma unroll
-        for (int i = 0; i < GS; ++i)
+        for (int i = 0; i < PPW; ++i)
 #pragma unroll
-            for (int jb = 0; jb < RB; ++jb)
-                af[i][jb] = bload8<V>(ars, static_cast<uint32_t>(min(jb * 16 + r, Rp - 1)) * rowb + kb, step_b(i));
-    };
-    if (cg < a.S) load_a(cg);
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int jb = 0; jb < RB; ++jb)
+                    af[i][h][jb] = bload8<V>(ars, static_cast<uint32_t>(min(jb * 16 + r, Rp - 1)) * rowb + 16 * kq,
+                                             static_cast<uint32_t>(2 * (pa + min(pair_of(i), pn - 1)) + h) * 64);
+    }
 
-    // 2. x fragments for all T rows (rows past T repeat row T-1; their
-    //    outputs are never used) and W fragments for all 64 columns.
+    // 2. Step pairs straight into this wave's ring slots: one instruction per
+    //    8 rows, 8 lanes a row covering its 128-byte line; the chunk a lane
+    //    fetches is XOR-swizzled by the row within its 16-row block, so the
+    //    chunk at position m of row rho is chunk m ^ sw(rho), sw(rho) =
+    //    (rho & 7) ^ (rho >> 3).  x rows past T repeat row T - 1 (their
+    //    outputs are never used).
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(T) * rowb);
     const __amdgpu_buffer_rsrc_t wrs =
         make_rsrc(static_cast<const uint16_t *>(a.W) + static_cast<size_t>(c0) * a.d_in, DCOLS * rowb);
-    uint32_t xo[TB];
+    uint32_t loff[L];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) xo[tb] = static_cast<uint32_t>(min(tb * 16 + r, T - 1)) * rowb + kb;
-    const uint32_t wo = static_cast<uint32_t>(r) * rowb + kb;
-    V xf[GS][TB];
-    V wf[GS][DCB];
-#pragma unroll
-    for (int i = 0; i < GS; ++i) {
-        const uint32_t sb = step_b(i);
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) xf[i][tb] = bload8<V>(xrs, xo[tb], sb);
-#pragma unroll
-        for (int c = 0; c < DCB; ++c) wf[i][c] = bload8<V>(wrs, wo, sb + c * 16 * rowb);
+    for (int g = 0; g < L; ++g) {
+        const int rho = 8 * (g & 1) + (lane >> 3);   // row within its 16-row block
+        const int chunk = (lane & 7) ^ (rho & 7) ^ (rho >> 3);
+        const int row = 8 * g + (lane >> 3);         // row of the slot: x rows first, then W
+        const int src = row < Ring::XROWS ? min(row, T - 1) : row - Ring::XROWS;
+        loff[g] = static_cast<uint32_t>(src) * rowb + chunk * 16;
     }
-
-    // 3. Base GEMM on the steps this wave holds.
-    f32x4_t acc[TB][DCB];
+    u32x4_t *ring = smem + wave * RS * Ring::UNITS;
+    // Byte offset of pair i of this wave within a row (clamped to the split).
+    auto pair_off = [&](int i) { return static_cast<uint32_t>(pa + min(pair_of(i), pn - 1)) * 128; };
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+    for (int i = 0; i < RS; ++i)
+        issue_pair(xrs, wrs, ring + (i % RS) * Ring::UNITS, loff, Ring::XROWS / 8, L, pair_off(i));
+    // Adapter index of token `lane` (every wave holds all T of them), used
+    // by the shrink at the end.
+    const int my_idx = idx[min(lane, T - 1)];
+
+    // 3. Base GEMM (and the shrink of slot cg) pair by pair.  Operand reads:
+    //    lane (r, kq) of half h takes row r of a block, chunk 4 h + kq, at
+    //    position (4 h + kq) ^ sw(r).
+    const int sw = (r & 7) ^ (r >> 3);
+    const int lo[2] = {r * 8 + ((0 + kq) ^ sw), r * 8 + ((4 + kq) ^ sw)};
+    f32x4_t acc[TB][DCB];
+    f32x4_t hacc[TB][RB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
         for (int c = 0; c < DCB; ++c) acc[tb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < GS; ++i) {
-        if (wave + NWK * i < nsq) {
+        for (int jb = 0; jb < RB; ++jb) hacc[tb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
+    for (int i = 0; i < PPW; ++i) {
+        // Loads issued after pair i so far: pairs i + 1 .. min(i + RS - 1,
+        // PPW - 1), and the token-index load (issued after pair RS - 1).
+        const int later = (i + RS - 1 < PPW - 1 ? i + RS - 1 : PPW - 1) - i;
+        const int extra = i < RS ? 1 : 0;
+        if (later == 0) {
+            if (extra) vm_wait<1>(); else vm_wait<0>();
+        } else if (later == 1) {
+            if (extra) vm_wait<L + 1>(); else vm_wait<L>();
+        } else if (later == 2 && 2 * L + 1 < 64) {
+            if (extra) vm_wait<(2 * L + 1) % 64>(); else vm_wait<(2 * L) % 64>();
+        } else {
+            vm_wait<0>();
+        }
+        const u32x4_t *slot = ring + (i % RS) * Ring::UNITS;
+        V xf[2][TB], wf[2][DCB];
 #pragma unroll
-                for (int c = 0; c < DCB; ++c) acc[tb][c] = E::mfma(xf[i][tb], wf[i][c], acc[tb][c]);
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) xf[h][tb] = __builtin_bit_cast(V, slot[tb * 128 + lo[h]]);
+#pragma unroll
+            for (int c = 0; c < DCB; ++c) wf[h][c] = __builtin_bit_cast(V, slot[(TB + c) * 128 + lo[h]]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (i + RS < PPW)
+            issue_pair(xrs, wrs, ring + (i % RS) * Ring::UNITS, loff, Ring::XROWS / 8, L, pair_off(i + RS));
+        if (pair_of(i) < pn) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int c = 0; c < DCB; ++c) acc[tb][c] = E::mfma(xf[h][tb], wf[h][c], acc[tb][c]);
+                if (shrink0) {
+#pragma unroll
+                    for (int jb = 0; jb < RB; ++jb) {
+                        const V am = (jb * 16 + r < Rp) ? af[i][h][jb] : zero8<V>();
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb) hacc[tb][jb] = E::mfma(xf[h][tb], am, hacc[tb][jb]);
+                    }
+                }
+            }
         }
     }
 
-    // 4. The 4 waves' sums in LDS, added in a fixed order (wave 0 + 1 + 2 +
-    //    3), stored as this split's partial sums, fragment order
-    //    [q][16-column block][tb][lane] (16 bytes a lane).
+    // 4. The 4 waves' sums in LDS (the ring is free once every wave is past
+    //    its last pair), added in a fixed order (wave 0 + 1 + 2 + 3), stored
+    //    as this split's partial sums, fragment order [q][16-column
+    //    block][tb][lane] (16 bytes a lane).
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
+    __syncthreads();
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -316,36 +415,16 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
         part[((static_cast<size_t>(q) * (a.d_out / 16) + c0 / 16 + c) * TB + tb) * 64 + lane] = v;
     }
 
-    // 5. Shrink: slots s = cg, cg + ncg, ... named by some token and active.
-    //    This split's part of h for all T rows, from the x fragments held;
-    //    the 4 waves' sums added in order; rows of the slot's tokens kept.
+    // 5. Shrink results: this split's part of h = x . A_s^T for the rows of
+    //    the tokens of slot s (fp32, by token, part q); the 4 waves' sums
+    //    added in order.
     float *hout = a.h + static_cast<size_t>(q) * T * Rp;
-    for (int s = cg; s < a.S; s += ncg) {
-        const unsigned long long mask = __ballot(lane < T && my_idx == s);
-        if (mask == 0) continue;
-        if (uniform(a.slots[s].state) != SLOT_ACTIVE) continue;
-        if (s != cg) load_a(s);
-        f32x4_t hacc[TB][RB];
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int jb = 0; jb < RB; ++jb) hacc[tb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < GS; ++i) {
-            if (wave + NWK * i < nsq) {
-#pragma unroll
-                for (int jb = 0; jb < RB; ++jb) {
-                    const V am = (jb * 16 + r < Rp) ? af[i][jb] : zero8<V>();
-#pragma unroll
-                    for (int tb = 0; tb < TB; ++tb) hacc[tb][jb] = E::mfma(xf[i][tb], am, hacc[tb][jb]);
-                }
-            }
-        }
+    auto store_h = [&](unsigned long long mask, const f32x4_t (&hc)[TB][RB]) {
         __syncthreads();  // red free
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int jb = 0; jb < RB; ++jb) red[((wave * TB + tb) * RB + jb) * 64 + lane] = hacc[tb][jb];
+            for (int jb = 0; jb < RB; ++jb) red[((wave * TB + tb) * RB + jb) * 64 + lane] = hc[tb][jb];
         __syncthreads();
         for (int f = wave; f < TB * RB; f += NWK) {
             f32x4_t v = red[f * 64 + lane];
@@ -353,11 +432,50 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int w = 1; w < NWK; ++w) v += red[(w * TB * RB + f) * 64 + lane];
             const int tb = f / RB, j = (f % RB) * 16 + r;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tb * 16 + kq * 4 + i;
-                if (j < Rp && t < T && ((mask >> t) & 1ull)) hout[static_cast<size_t>(t) * Rp + j] = v[i];
+            for (int e = 0; e < 4; ++e) {
+                const int t = tb * 16 + kq * 4 + e;
+                if (j < Rp && t < T && ((mask >> t) & 1ull)) hout[static_cast<size_t>(t) * Rp + j] = v[e];
             }
         }
+    };
+    if (shrink0) {
+        const unsigned long long mask = __ballot(lane < T && my_idx == cg);
+        if (mask != 0 && uniform(a.slots[cg].state) == SLOT_ACTIVE) store_h(mask, hacc);
+    }
+    // Slots cg + ncg, cg + 2 ncg, ... (pools of more slots than column
+    // groups): x fragments read again, straight from global memory.
+    for (int s = cg + ncg; s < a.S; s += ncg) {
+        const unsigned long long mask = __ballot(lane < T && my_idx == s);
+        if (mask == 0) continue;
+        if (uniform(a.slots[s].state) != SLOT_ACTIVE) continue;
+        const __amdgpu_buffer_rsrc_t ars =
+            make_rsrc(static_cast<const uint16_t *>(a.A_slab) + static_cast<size_t>(s) * Rp * a.d_in, Rp * rowb);
+        f32x4_t hc[TB][RB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int jb = 0; jb < RB; ++jb) hc[tb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < PPW; ++i) {
+            if (pair_of(i) >= pn) break;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t sb = static_cast<uint32_t>(2 * (pa + pair_of(i)) + h) * 64;
+                V xv[TB], av[RB];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    xv[tb] = bload8<V>(xrs, static_cast<uint32_t>(min(tb * 16 + r, T - 1)) * rowb + 16 * kq, sb);
+#pragma unroll
+                for (int jb = 0; jb < RB; ++jb)
+                    av[jb] = bload8<V>(ars, static_cast<uint32_t>(min(jb * 16 + r, Rp - 1)) * rowb + 16 * kq, sb);
+#pragma unroll
+                for (int jb = 0; jb < RB; ++jb) {
+                    const V am = (jb * 16 + r < Rp) ? av[jb] : zero8<V>();
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) hc[tb][jb] = E::mfma(xv[tb], am, hc[tb][jb]);
+                }
+            }
+        }
+        store_h(mask, hc);
     }
 }
 
@@ -548,15 +666,16 @@ int decode_token_blocks(int T) {
 }
 
 int decode_splits(int T, int d_in) {
-    // Every GEMM wave holds all its steps: at most NWK x DSTEPS_PER_WAVE k
-    // steps per split, at least 4 splits (64-column workgroups: d_out / 16
-    // of them at d_out = 4096, one per CU); 0 beyond MAX_DSPLIT splits.
+    // Each GEMM wave takes at most DPAIRS_PER_WAVE step pairs (64 k each):
+    // at most NWK x DPAIRS_PER_WAVE pairs per split, at least 4 splits
+    // (64-column workgroups: d_out / 16 of them at d_out = 4096, one per CU);
+    // 0 beyond MAX_DSPLIT splits.  d_in is a multiple of 64.
     (void)T;
-    const int kst = d_in / 32;
-    const int per = NWK * DSTEPS_PER_WAVE;
-    int s = (kst + per - 1) / per;
+    const int kp = d_in / 64;
+    const int per = NWK * DPAIRS_PER_WAVE;
+    int s = (kp + per - 1) / per;
     if (s < 4) s = 4;
-    if (s > kst) s = kst;  // every split keeps at least one k step
+    if (s > kp) s = kp;  // every split keeps at least one pair
     return s <= MAX_DSPLIT ? s : 0;
 }
 
