@@ -17,7 +17,7 @@
 //   T rows.
 //   * Operands go from global memory straight into LDS (buffer_load ... lds),
 //     one instruction per 8 rows with 8 lanes covering each row's 128-byte
-//     line, into a per-wave ring of 2-3 pair slots (128 KiB in all); the
+//     line, into a per-wave ring of 2-4 pair slots (up to 160 KiB); the
 //     MFMA operands are read back from XOR-swizzled rows without bank
 //     conflicts.  Each wave waits only for its own loads (no barrier in the
 //     loop).  The A rows of slot c are requested first, into registers
@@ -228,6 +228,22 @@ __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Waits until at most later * L + extra loads are outstanding (later <= 3;
+// the branches fold away when the arguments are constants).
+template <int L>
+__device__ __forceinline__ void wait_loads(int later, int extra) {
+    static_assert(3 * L + 1 < 64, "vmcnt is 6 bits");
+    if (later == 0) {
+        if (extra) vm_wait<1>(); else vm_wait<0>();
+    } else if (later == 1) {
+        if (extra) vm_wait<L + 1>(); else vm_wait<L>();
+    } else if (later == 2) {
+        if (extra) vm_wait<2 * L + 1>(); else vm_wait<2 * L>();
+    } else {
+        if (extra) vm_wait<3 * L + 1>(); else vm_wait<3 * L>();
+    }
+}
+
 // One step pair into a ring slot: nx x-row instructions then W-row ones up
 // to nl, instruction g filling the slot's 16-byte units 64 g .. 64 g + 63.
 __device__ __forceinline__ void issue_pair(const __amdgpu_buffer_rsrc_t &xrs, const __amdgpu_buffer_rsrc_t &wrs,
@@ -243,13 +259,13 @@ __device__ __forceinline__ void issue_pair(const __amdgpu_buffer_rsrc_t &xrs, co
 
 // Ring slots per wave for TB token blocks: a slot holds one step pair of x
 // (16 TB rows) and W (64 rows), 128 bytes a row; the ring of the 4 waves
-// stays within 128 KiB.
+// stays within the 160 KiB of LDS.
 template <int TB>
 struct DecRing {
     static constexpr int XROWS = TB * 16;
     static constexpr int UNITS = (XROWS + DCOLS) * 8;          // 16-byte units per slot
     static constexpr int LOADS = (XROWS + DCOLS) / 8;          // load instructions per slot
-    static constexpr int FIT = (128 * 1024 / 16) / (NWK * UNITS);
+    static constexpr int FIT = (160 * 1024 / 16) / (NWK * UNITS);
     static constexpr int SLOTS = FIT < DPAIRS_PER_WAVE ? FIT : DPAIRS_PER_WAVE;
 };
 
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int PPW = DPAIRS_PER_WAVE;
     constexpr int RS = Ring::SLOTS;
     constexpr int L = Ring::LOADS;
-    static_assert(RS >= 1, "ring");
+    static_assert(RS >= 1 && RS <= 4, "ring");
     static_assert(NWK * NB * 64 <= NWK * RS * Ring::UNITS, "cross-wave sums fit in the ring");
     // Per-wave rings of step pairs; after the main loop, the cross-wave sums.
     __shared__ u32x4_t smem[NWK * RS * Ring::UNITS];
@@ -352,16 +368,7 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
         // Loads issued after pair i so far: pairs i + 1 .. min(i + RS - 1,
         // PPW - 1), and the token-index load (issued after pair RS - 1).
         const int later = (i + RS - 1 < PPW - 1 ? i + RS - 1 : PPW - 1) - i;
-        const int extra = i < RS ? 1 : 0;
-        if (later == 0) {
-            if (extra) vm_wait<1>(); else vm_wait<0>();
-        } else if (later == 1) {
-            if (extra) vm_wait<L + 1>(); else vm_wait<L>();
-        } else if (later == 2 && 2 * L + 1 < 64) {
-            if (extra) vm_wait<(2 * L + 1) % 64>(); else vm_wait<(2 * L) % 64>();
-        } else {
-            vm_wait<0>();
-        }
+        wait_loads<L>(later, i < RS ? 1 : 0);
         const u32x4_t *slot = ring + (i % RS) * Ring::UNITS;
         V xf[2][TB], wf[2][DCB];
 #pragma unroll
@@ -532,9 +539,10 @@ __global__ __launch_bounds__((NWK + 1) * 64) void k_decode_epilogue(ApplyArgs a,
         for (int qb = 0; qb < 2 * RB; ++qb) bw[i][qb] = *reinterpret_cast<const u32x4_t *>(bp + min(8 * qb, Rp - 8));
         sc[i] = a.slots[kc].scale;
     }
-    // Splits are taken SQ at a time (all of them at once for d_in <= 4096),
-    // each group's loads in flight together, and added in split order.
-    constexpr int SQ = 4;
+    // Splits are taken SQ at a time (4: all of them at once for d_in <=
+    // 4096; 2 at ranks above 32, for registers), each group's loads in
+    // flight together, and added in split order.
+    constexpr int SQ = RB >= 3 ? 2 : 4;
     const f32x4_t *part = reinterpret_cast<const f32x4_t *>(d.part) + (static_cast<size_t>(nb) * TB + tb) * 64 + lane;
     const size_t qstride = static_cast<size_t>(a.d_out / 16) * TB * 64;
     const int hq_n = T * Rp / 4;
@@ -545,14 +553,16 @@ __global__ __launch_bounds__((NWK + 1) * 64) void k_decode_epilogue(ApplyArgs a,
     for (int q0 = 0; q0 < d.splits; q0 += SQ) {
         f32x4_t pv[SQ];
         float4 hv[HQ][SQ];
+        // Unconditional loads (split index clamped; the repeats are not
+        // added), so the wait counts stay exact.
 #pragma unroll
-        for (int u = 0; u < SQ; ++u)
-            if (q0 + u < d.splits) pv[u] = part[(q0 + u) * qstride];
+        for (int u = 0; u < SQ; ++u) pv[u] = part[min(q0 + u, d.splits - 1) * qstride];
 #pragma unroll
         for (int m = 0; m < HQ; ++m)
 #pragma unroll
             for (int u = 0; u < SQ; ++u)
-                if (q0 + u < d.splits) hv[m][u] = hp[(q0 + u) * pstride + min(tid + m * NWK * 64, hq_n - 1)];
+                hv[m][u] = hp[min(q0 + u, d.splits - 1) * pstride + min(tid + m * NWK * 64, hq_n - 1)];
+        asm volatile("" ::: "memory");  // every load of the group is issued before the first add
         if (q0 == 0) {
             acc = pv[0];
 #pragma unroll
@@ -610,10 +620,11 @@ __global__ __launch_bounds__((NWK + 1) * 64) void k_decode_epilogue(ApplyArgs a,
 #pragma unroll
             for (int qb = 0; qb < 2 * RB; ++qb) {
                 if (8 * qb < Rp) {
+                    const u32x4_t bq = bw[i][qb];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        dsum += hrow[8 * qb + 2 * e] * E::to_f(static_cast<raw>(bw[i][qb][e] & 0xFFFFu));
-                        dsum += hrow[8 * qb + 2 * e + 1] * E::to_f(static_cast<raw>(bw[i][qb][e] >> 16));
+                        dsum += hrow[8 * qb + 2 * e] * E::to_f(static_cast<raw>(bq[e] & 0xFFFFu));
+                        dsum += hrow[8 * qb + 2 * e + 1] * E::to_f(static_cast<raw>(bq[e] >> 16));
                     }
                 }
             }

@@ -84,7 +84,11 @@ def _small_case(dtype, T, d_in, d_out, S, R, seed):
 # register-staged tiles (ragged d_in / d_out), the split-K 256-row tiles
 # (T 65 .. 2047 with d_in, d_out multiples of 128; 4 and 2 splits here) and
 # the unsplit 256 x 256 tiles (T >= 2048), each with a ragged last tile.
+# Decode calls also cover pools beyond the epilogue's small-pool B tile (S R
+# > 1024) and beyond 64 slots (routing loads each token's slot entry; the GEMM
+# takes slots past its column groups in a second pass).
 @pytest.mark.parametrize("T,d_in,d_out,S,R", [(1, 64, 64, 1, 1), (37, 128, 192, 5, 8),
+                                               (50, 256, 128, 20, 64), (64, 128, 64, 70, 16),
                                                (77, 192, 128, 9, 16), (300, 256, 320, 17, 64),
                                                (513, 64, 128, 40, 24), (200, 1024, 384, 7, 16),
                                                (1000, 512, 512, 11, 32), (2100, 256, 256, 3, 8)])
