@@ -39,7 +39,8 @@ CSRC = os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc")
 KERNELS = {
     "decode": ("k_decode_gemm", ["gemm_decode.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
     "tiled": ("k_gemm_tiled", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
-    "big": ("k_gemm_big", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
+    "split": ("k_gemm_lds<128, split>", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
+    "big": ("k_gemm_lds<256>", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
 }
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -366,6 +367,8 @@ def main():
             kind = "decode"
         elif c0.T >= 2048 and c0.d_out % 256 == 0 and c0.d_in % 128 == 0:
             kind = "big"
+        elif c0.d_out % 128 == 0 and c0.d_in % 128 == 0:
+            kind = "split"
         else:
             kind = "tiled"
         roof["kernel"] = KERNELS[kind][0]
