@@ -163,10 +163,30 @@ def setup(args, L):
 # timing
 # ----------------------------------------------------------------------------
 
+# Steps of several calls over one batch (prefill's two projections, the
+# stack's 224 linears) resolve the token -> adapter routing once per step
+# (lora_plan_route) and run every linear on it (lora_apply_routed); a step of
+# one call, or calls of at most 64 tokens (whose routing rides the decode
+# epilogue), calls lora_apply.  PLAN holds the plan handle when in use.
+PLAN = {"handle": None}
+
+
+def use_plan(steps, per_call):
+    return not per_call and len(steps[0]) > 1 and steps[0][0].T > 64
+
+
 def run_steps(L, steps, n, start=0):
+    plan = PLAN["handle"]
     for i in range(start, start + n):
-        for c in steps[i % len(steps)]:
-            L.lora_apply(c.pool, c.x, c.W, c.idx, c.T, c.y)
+        step = steps[i % len(steps)]
+        if plan is not None:
+            c0 = step[0]
+            L.lora_plan_route(plan, c0.pool, c0.idx, c0.T)
+            for c in step:
+                L.lora_apply_routed(c.pool, plan, c.x, c.W, c.y)
+        else:
+            for c in step:
+                L.lora_apply(c.pool, c.x, c.W, c.idx, c.T, c.y)
 
 
 def timed(L, steps, K):
@@ -297,6 +317,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-stage pass")
+    ap.add_argument("--route-per-call", action="store_true",
+                    help="route every call (lora_apply) instead of once per step (lora_plan_route)")
     ap.add_argument("--theta-sweep", action="store_true",
                     help="run the fused/separate threshold sweep instead of the bench step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -318,6 +340,8 @@ def main():
         return
 
     w, steps, desc = setup(args, L)
+    if use_plan(steps, args.route_per_call):
+        PLAN["handle"] = L.lora_plan_create(w.T, w.S)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -398,6 +422,7 @@ def main():
         "config": {"workload": desc, "tokens_per_step": tokens_per_step,
                    "calls_per_step": len(calls), "weight_copies": len(steps),
                    "policy": ["auto", "fused", "separate"][calls[0].policy], "theta": calls[0].theta,
+                   "routing": "once per step (lora_plan_route)" if PLAN["handle"] is not None else "per call",
                    "step_bytes_alg": step_bytes, "step_flops_alg": step_flops},
         "step_roofline": {"hbm_GBs": step_bytes / step_s / 1e9,
                           "hbm_frac": step_bytes / step_s / 1e9 / HBM_PEAK_GBS,

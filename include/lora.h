@@ -61,6 +61,7 @@ extern "C" {
 /* ---------------------------------------------------------------- types -- */
 
 typedef struct lora_pool_s *lora_pool; /* opaque; owned by the library */
+typedef struct lora_plan_s *lora_plan; /* opaque routing plan; owned by the library */
 
 typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
 
@@ -209,6 +210,47 @@ int lora_apply(lora_pool p, const void *x, const void *W_base,
 int lora_route(lora_pool p, const int32_t *token_adapter_idx, int n_tokens,
                int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *segs,
                int32_t *n_seg, void *stream);
+
+/* ------------------------------------------------- route once per step -- */
+
+/* A routing plan: the tenant-to-adapter mapping of one batch resolved once,
+ * at entry, and reused by every linear of the step instead of being looked
+ * up again on the hot path ["xpshop.cn article 492", 二/三: the handle is
+ * resolved at request entry; "LLM 多 LoRA 推理服务工程 2026", routing layer:
+ * bucketing per batch].  The plan holds a device copy of the token indices
+ * and the routing arrays (the same ones lora_apply builds), sized for
+ * max_tokens and n_slots.  Allocates once, here.
+ * Errors: LORA_EINVAL (sizes out of range, out == NULL), LORA_ENOMEM, LORA_EHIP. */
+int lora_plan_create(int max_tokens, int n_slots, lora_plan *out);
+
+/* Waits for the plan's enqueued routing, then frees it.  The caller must not
+ * destroy a plan that applies still to run on another stream read. */
+int lora_plan_destroy(lora_plan plan);
+
+/* Route a batch into the plan, asynchronously on `stream`, with pool p's slot
+ * table and fused/separate policy (p->n_slots must equal the plan's).  Copies
+ * token_adapter_idx (device int32 [n_tokens]) into the plan, then runs the
+ * routing kernel.  Invalid tokens are counted once, here, on p's error
+ * counter.  The plan records p's active slots, policy and threshold at this
+ * call; lora_apply_routed checks them.
+ * Errors: LORA_EINVAL, LORA_ETOKENS (n_tokens > the plan's max_tokens),
+ * LORA_EMISMATCH (slot count differs), LORA_EHIP. */
+int lora_plan_route(lora_plan plan, lora_pool p, const int32_t *token_adapter_idx, int n_tokens,
+                    void *stream);
+
+/* lora_apply for the plan's batch (n_tokens = the plan's), without the
+ * routing pass: the plan's routing and token indices are used.  Must follow
+ * the lora_plan_route on the same stream (or an event that orders them).
+ * The result equals lora_apply's with the same indices bit for bit.  Pool p
+ * must match the routing pool in slot count, active slots, policy and
+ * threshold (as of the route call), else LORA_EMISMATCH and nothing is
+ * enqueued: its adapters (A, B, scales) may differ -- one plan serves the
+ * pools of every linear of a model.  Leaves p's last-call statistics and
+ * error counter unchanged.
+ * Errors (host-side, nothing enqueued): LORA_EINVAL (no routed batch,
+ * pointers), LORA_ETOKENS, LORA_EMISMATCH, LORA_EHIP. */
+int lora_apply_routed(lora_pool p, lora_plan plan, const void *x, const void *W_base, void *y,
+                      void *stream);
 
 /* ---------------------------------------------------------- observation -- */
 

@@ -103,6 +103,22 @@ struct lora_pool_s {
     lora_pool_s(int n_slots, int max_rank, uint64_t slot_bytes) : book(n_slots, max_rank, slot_bytes) {}
 };
 
+struct lora_plan_s {
+    int device = 0;
+    int max_T = 0, S = 0;
+    char *mem = nullptr;        // one device allocation: the index copy and the routing arrays
+    int32_t *idx = nullptr;     // [max_T] copy of the routed batch's token indices
+    lora::RouteOut ro{};
+    hipStream_t internal = nullptr;
+    // The routed batch and what its routing depended on (pool state at
+    // lora_plan_route).
+    int T = -1;
+    int policy = 0, theta = 0;
+    std::vector<uint8_t> active;  // [S] slot was ACTIVE
+    hipEvent_t done = nullptr;    // after the routing was enqueued
+    hipStream_t done_stream = nullptr;
+};
+
 namespace {
 
 void free_profile(lora_pool p) {
@@ -150,6 +166,88 @@ hipError_t drain_inflight(lora_pool p) {
 }
 
 bool aligned(const void *ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace
+
+namespace {
+
+// The body of lora_apply and lora_apply_routed: pool mutex held, pool device
+// current, arguments checked.  `pre`: routing already in place (a plan's), or
+// nullptr to route here.
+int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *token_adapter_idx, int n_tokens,
+                 void *y, hipStream_t st, const lora::RouteOut *pre) {
+    lora_pool_s::ProfSet *ps = (p->prof_used < p->prof.size()) ? &p->prof[p->prof_used++] : nullptr;
+    auto mark = [&](int i) { return ps ? hipEventRecord(ps->e[i], st) : hipSuccess; };
+    lora::LaunchEvents kev{};
+    if (ps) kev = lora::LaunchEvents{ps->e[5], ps->e[6]};
+
+    lora::ApplyArgs a{};
+    a.dtype = p->dtype;
+    a.T = n_tokens;
+    a.d_in = p->d_in;
+    a.d_out = p->d_out;
+    a.S = p->S;
+    a.R = p->Rp;
+    a.x = x;
+    a.W = W_base;
+    a.y = y;
+    a.A_slab = p->A_slab;
+    a.B_slab = p->B_slab;
+    a.slots = p->slots_dev;
+    a.h = p->h;
+    a.h_parts = 1;
+    // Routing arrays: the plan's (routed already), or the pool's own.
+    const lora::RouteOut &rsrc = pre ? *pre : p->ro;
+    a.rv = lora::RouteView{rsrc.perm, rsrc.pos_seg, rsrc.tok_pos, rsrc.tok_seg, rsrc.segs, rsrc.tiles, rsrc.n_tiles};
+    a.tiles_bound = lora::max_tiles(n_tokens, p->S);
+    a.policy = p->policy;
+    const bool half = p->esz == 2;
+    // Every LoRA bucket is FUSED under the FUSED policy, and under AUTO with
+    // threshold 0 (a bucket holds at least one token): no residual launch then.
+    const bool any_separate = !(p->policy == LORA_MODE_FUSED || (p->policy == LORA_MODE_AUTO && p->theta == 0));
+
+    HIP_TRY(mark(0));
+    const int dsplits = (half && n_tokens <= lora::DECODE_MAX_T) ? lora::decode_splits(n_tokens, p->d_in) : 0;
+    if (dsplits > 0) {
+        // Split-K GEMM with the shrink, then the epilogue, which routes,
+        // sums the splits and adds the fused expand.
+        lora::DecodeArgs d{};
+        d.splits = dsplits;
+        d.max_rank = p->R;
+        d.theta = p->theta;
+        d.part = p->part;
+        a.h_parts = dsplits;
+        a.h_by_token = 1;
+        HIP_TRY(mark(1));
+        HIP_TRY(mark(2));
+        // A routed call publishes into the pool's arrays (nobody reads them)
+        // and leaves its statistics and error counter alone.
+        lora::RouteOut out = p->ro;
+        if (pre) out.stats = nullptr, out.err = nullptr;
+        HIP_TRY(lora::launch_decode(a, d, token_adapter_idx, out, st, kev));
+    } else {
+        if (!pre)
+            HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
+                                       p->ro, st));
+        HIP_TRY(mark(1));
+        if (half) a.h_parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound);
+        HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
+        HIP_TRY(mark(2));
+        if (half) {
+            HIP_TRY(lora::launch_gemm_tiled(a, p->part, st, kev));
+        } else {
+            HIP_TRY(lora::launch_base_gemm(a, st));
+            HIP_TRY(mark(5));
+            HIP_TRY(mark(6));
+        }
+    }
+    HIP_TRY(mark(3));
+    if (any_separate) HIP_TRY(half ? lora::launch_expand_sep16(a, st) : lora::launch_expand_separate(a, st));
+    HIP_TRY(mark(4));
+    HIP_TRY(record_inflight(p, st));
+    return LORA_OK;
+}
+
 
 }  // namespace
 
@@ -390,71 +488,7 @@ int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *to
     std::lock_guard<std::mutex> lk(p->mu);
     DeviceGuard g(p->device);
     HIP_TRY(g.error());
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    lora_pool_s::ProfSet *ps = (p->prof_used < p->prof.size()) ? &p->prof[p->prof_used++] : nullptr;
-    auto mark = [&](int i) { return ps ? hipEventRecord(ps->e[i], st) : hipSuccess; };
-    lora::LaunchEvents kev{};
-    if (ps) kev = lora::LaunchEvents{ps->e[5], ps->e[6]};
-
-    lora::ApplyArgs a{};
-    a.dtype = p->dtype;
-    a.T = n_tokens;
-    a.d_in = p->d_in;
-    a.d_out = p->d_out;
-    a.S = p->S;
-    a.R = p->Rp;
-    a.x = x;
-    a.W = W_base;
-    a.y = y;
-    a.A_slab = p->A_slab;
-    a.B_slab = p->B_slab;
-    a.slots = p->slots_dev;
-    a.h = p->h;
-    a.h_parts = 1;
-    a.rv = lora::RouteView{p->ro.perm, p->ro.pos_seg, p->ro.tok_pos, p->ro.tok_seg,
-                           p->ro.segs, p->ro.tiles, p->ro.n_tiles};
-    a.tiles_bound = lora::max_tiles(n_tokens, p->S);
-    a.policy = p->policy;
-    const bool half = p->esz == 2;
-    // Every LoRA bucket is FUSED under the FUSED policy, and under AUTO with
-    // threshold 0 (a bucket holds at least one token): no residual launch then.
-    const bool any_separate = !(p->policy == LORA_MODE_FUSED || (p->policy == LORA_MODE_AUTO && p->theta == 0));
-
-    HIP_TRY(mark(0));
-    const int dsplits = (half && n_tokens <= lora::DECODE_MAX_T) ? lora::decode_splits(n_tokens, p->d_in) : 0;
-    if (dsplits > 0) {
-        // Split-K GEMM with the shrink, then the epilogue, which routes,
-        // sums the splits and adds the fused expand.
-        lora::DecodeArgs d{};
-        d.splits = dsplits;
-        d.max_rank = p->R;
-        d.theta = p->theta;
-        d.part = p->part;
-        a.h_parts = dsplits;
-        a.h_by_token = 1;
-        HIP_TRY(mark(1));
-        HIP_TRY(mark(2));
-        HIP_TRY(lora::launch_decode(a, d, token_adapter_idx, p->ro, st, kev));
-    } else {
-        HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
-                                   p->ro, st));
-        HIP_TRY(mark(1));
-        if (half) a.h_parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound);
-        HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
-        HIP_TRY(mark(2));
-        if (half) {
-            HIP_TRY(lora::launch_gemm_tiled(a, p->part, st, kev));
-        } else {
-            HIP_TRY(lora::launch_base_gemm(a, st));
-            HIP_TRY(mark(5));
-            HIP_TRY(mark(6));
-        }
-    }
-    HIP_TRY(mark(3));
-    if (any_separate) HIP_TRY(half ? lora::launch_expand_sep16(a, st) : lora::launch_expand_separate(a, st));
-    HIP_TRY(mark(4));
-    HIP_TRY(record_inflight(p, st));
-    return LORA_OK;
+    return apply_locked(p, x, W_base, token_adapter_idx, n_tokens, y, static_cast<hipStream_t>(stream), nullptr);
 }
 
 int lora_route(lora_pool p, const int32_t *token_adapter_idx, int n_tokens, int32_t *counts, int32_t *offsets,
@@ -479,6 +513,128 @@ int lora_route(lora_pool p, const int32_t *token_adapter_idx, int n_tokens, int3
                                st));
     HIP_TRY(record_inflight(p, st));
     return LORA_OK;
+}
+
+int lora_plan_create(int max_tokens, int n_slots, lora_plan *out) {
+    if (out == nullptr) return LORA_EINVAL;
+    *out = nullptr;
+    if (max_tokens < 1 || n_slots < 1 || n_slots > LORA_MAX_SLOTS) return LORA_EINVAL;
+    lora_plan pl = new (std::nothrow) lora_plan_s;
+    if (pl == nullptr) return LORA_ENOMEM;
+    pl->max_T = max_tokens;
+    pl->S = n_slots;
+    hipError_t e = hipGetDevice(&pl->device);
+    // Carve the index copy and the routing arrays out of one allocation.
+    const size_t T = static_cast<size_t>(max_tokens), S = static_cast<size_t>(n_slots);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const size_t o_idx = take(T * 4);
+    const size_t o_counts = take((S + 2) * 4);
+    const size_t o_offsets = take((S + 3) * 4);
+    const size_t o_perm = take(T * 4);
+    const size_t o_segs = take((S + 2) * 16);
+    const size_t o_nseg = take(4);
+    const size_t o_posseg = take(T * 4);
+    const size_t o_tokpos = take(T * 4);
+    const size_t o_tokseg = take(T * 4);
+    const size_t o_tiles = take(static_cast<size_t>(lora::max_tiles(max_tokens, n_slots)) * 8);
+    const size_t o_ntiles = take(4);
+    const size_t o_stats = take(sizeof(lora::DevStats));
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&pl->mem), off);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&pl->internal, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipMemsetAsync(pl->mem, 0, off, pl->internal);
+    if (e == hipSuccess) e = hipStreamSynchronize(pl->internal);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        const int rc = (e == hipErrorOutOfMemory) ? LORA_ENOMEM : hip_fail(e);
+        lora_plan_destroy(pl);
+        return rc;
+    }
+    char *m = pl->mem;
+    pl->idx = reinterpret_cast<int32_t *>(m + o_idx);
+    pl->ro.counts = reinterpret_cast<int32_t *>(m + o_counts);
+    pl->ro.offsets = reinterpret_cast<int32_t *>(m + o_offsets);
+    pl->ro.perm = reinterpret_cast<int32_t *>(m + o_perm);
+    pl->ro.segs = reinterpret_cast<int32_t *>(m + o_segs);
+    pl->ro.n_seg = reinterpret_cast<int32_t *>(m + o_nseg);
+    pl->ro.pos_seg = reinterpret_cast<int32_t *>(m + o_posseg);
+    pl->ro.tok_pos = reinterpret_cast<int32_t *>(m + o_tokpos);
+    pl->ro.tok_seg = reinterpret_cast<int32_t *>(m + o_tokseg);
+    pl->ro.tiles = reinterpret_cast<int32_t *>(m + o_tiles);
+    pl->ro.n_tiles = reinterpret_cast<int32_t *>(m + o_ntiles);
+    pl->ro.stats = reinterpret_cast<lora::DevStats *>(m + o_stats);
+    pl->ro.err = nullptr;  // set to the routing pool's counter per route
+    *out = pl;
+    return LORA_OK;
+}
+
+int lora_plan_destroy(lora_plan plan) {
+    if (plan == nullptr) return LORA_OK;
+    int rc = LORA_OK;
+    DeviceGuard g(plan->device);
+    if (plan->done_stream != nullptr) {
+        const hipError_t e = hipEventSynchronize(plan->done);
+        if (e != hipSuccess) rc = hip_fail(e);
+    }
+    if (plan->done) (void)hipEventDestroy(plan->done);
+    if (plan->mem) (void)hipFree(plan->mem);
+    if (plan->internal) (void)hipStreamDestroy(plan->internal);
+    delete plan;
+    return rc;
+}
+
+int lora_plan_route(lora_plan plan, lora_pool p, const int32_t *token_adapter_idx, int n_tokens, void *stream) {
+    if (plan == nullptr || p == nullptr || n_tokens < 0) return LORA_EINVAL;
+    if (n_tokens > plan->max_T || n_tokens > p->max_T) return LORA_ETOKENS;
+    if (n_tokens > 0 && (token_adapter_idx == nullptr || !aligned(token_adapter_idx, 4))) return LORA_EINVAL;
+    if (p->S != plan->S || p->device != plan->device) return LORA_EMISMATCH;
+    std::lock_guard<std::mutex> lk(p->mu);
+    DeviceGuard g(p->device);
+    HIP_TRY(g.error());
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    plan->T = -1;
+    if (n_tokens > 0) {
+        HIP_TRY(hipMemcpyAsync(plan->idx, token_adapter_idx, static_cast<size_t>(n_tokens) * 4,
+                               hipMemcpyDeviceToDevice, st));
+        lora::RouteOut ro = plan->ro;
+        ro.err = p->ro.err;  // invalid tokens counted once, on the routing pool
+        HIP_TRY(lora::launch_route(plan->idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta, ro, st));
+        HIP_TRY(record_inflight(p, st));
+    }
+    HIP_TRY(hipEventRecord(plan->done, st));
+    plan->done_stream = st;
+    plan->policy = p->policy;
+    plan->theta = p->theta;
+    plan->active.assign(static_cast<size_t>(p->S), 0);
+    for (int i = 0; i < p->S; ++i) plan->active[i] = p->book.slot(i).state == lora::SlotState::Active ? 1 : 0;
+    plan->T = n_tokens;
+    return LORA_OK;
+}
+
+int lora_apply_routed(lora_pool p, lora_plan plan, const void *x, const void *W_base, void *y, void *stream) {
+    if (p == nullptr || plan == nullptr || plan->T < 0) return LORA_EINVAL;
+    const int n_tokens = plan->T;
+    if (n_tokens == 0) return LORA_OK;
+    if (n_tokens > p->max_T) return LORA_ETOKENS;
+    if (x == nullptr || W_base == nullptr || y == nullptr) return LORA_EINVAL;
+    const size_t al = (p->esz == 2) ? 16 : 4;
+    if (!aligned(x, al) || !aligned(W_base, al) || !aligned(y, al)) return LORA_EINVAL;
+    if (x == y) return LORA_EINVAL;
+
+    std::lock_guard<std::mutex> lk(p->mu);
+    // The plan's routing holds for this pool only if every input of the
+    // routing matches: slot count, which slots are ACTIVE, policy, threshold.
+    if (p->S != plan->S || p->device != plan->device || p->policy != plan->policy || p->theta != plan->theta)
+        return LORA_EMISMATCH;
+    for (int i = 0; i < p->S; ++i)
+        if ((p->book.slot(i).state == lora::SlotState::Active ? 1 : 0) != plan->active[i]) return LORA_EMISMATCH;
+    DeviceGuard g(p->device);
+    HIP_TRY(g.error());
+    return apply_locked(p, x, W_base, plan->idx, n_tokens, y, static_cast<hipStream_t>(stream), &plan->ro);
 }
 
 int lora_pool_stats(lora_pool p, lora_stats *out) {

@@ -210,8 +210,8 @@ __device__ __forceinline__ void publish_route(const SmallRoute &sr, int T, const
         st.invalid_tokens = sr.stat[3];
         st.rows_padded = sr.stat[4];
         st.rows_true = sr.stat[5];
-        *out.stats = st;
-        if (sr.stat[3] > 0) atomicAdd(out.err, static_cast<unsigned long long>(sr.stat[3]));
+        if (out.stats) *out.stats = st;
+        if (out.err && sr.stat[3] > 0) atomicAdd(out.err, static_cast<unsigned long long>(sr.stat[3]));
     }
 }
 

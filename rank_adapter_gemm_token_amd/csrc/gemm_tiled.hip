@@ -138,9 +138,9 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
 // Which 16-byte chunk a lane fetches is XOR-swizzled by row, so the chunk in
 // position m of row rho is chunk m ^ sw(rho), sw(rho) = (rho & 7) ^ (rho >>
 // 3); the MFMA operand reads (16 rows of one chunk at a time) then hit
-// distinct banks.  Two LDS buffers (separate arrays, so the compiler can tell
-// a stage's reads from the next stage's loads): stage s + 1 is loaded while
-// stage s is multiplied, one barrier a stage.
+// distinct banks.  Two or three LDS buffers (separate arrays, so the compiler
+// can tell a stage's reads from the next stages' loads): stages s + 1 (and s
+// + 2) are loaded while stage s is multiplied, one barrier a stage.
 //
 // SPLIT = false (calls of >= 2048 tokens): all of d_in, then the fused
 // expand and the scatter to token order in the epilogue.
@@ -159,8 +159,12 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     constexpr int BOFF = 16 * RBU;       // W row blocks follow the 16 x row blocks
     constexpr int NBW = BN / 16;         // W row blocks per stage
     constexpr int BLD = NBW / 2;         // W load instructions per W wave (4 waves)
+    // Stage buffers: three at BN = 128 (two stages in flight while one is
+    // multiplied, 144 KiB), two at BN = 256 (128 KiB).
+    constexpr int NBUF = BN == 128 ? 3 : 2;
     __shared__ u32x4_t lds0[(16 + NBW) * RBU];
     __shared__ u32x4_t lds1[(16 + NBW) * RBU];
+    __shared__ u32x4_t lds2[NBUF == 3 ? (16 + NBW) * RBU : 1];
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -246,23 +250,51 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
             }
         }
     };
-    // Waits for this wave's loads, then for every wave's (the barrier also
-    // means the other buffer is no longer read).
-    auto sync_stage = [&]() {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Waits for this wave's loads of the stage about to be multiplied (all
+    // of them, or all but the next stage's when that one is in flight), then
+    // for every wave's; the barrier also means that the buffer the next
+    // issue writes is no longer read.
+    auto sync_stage = [&](bool next_in_flight) {
+        if (!next_in_flight) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else if (xw) {
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        } else {
+            static_assert(BLD == 4 || BLD == 8, "W-wave load count");
+            if (BLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        }
         __syncthreads();
     };
 
     const int nst = s_end - s_beg;
-    issue(s_beg, lds0);
-    for (int j = 0; j < nst; j += 2) {
-        sync_stage();
-        if (j + 1 < nst) issue(s_beg + j + 1, lds1);
-        compute(lds0);
-        if (j + 1 < nst) {
-            sync_stage();
-            if (j + 2 < nst) issue(s_beg + j + 2, lds0);
+    if (NBUF == 2) {
+        issue(s_beg, lds0);
+        for (int j = 0; j < nst; j += 2) {
+            sync_stage(false);
+            if (j + 1 < nst) issue(s_beg + j + 1, lds1);
+            compute(lds0);
+            if (j + 1 < nst) {
+                sync_stage(false);
+                if (j + 2 < nst) issue(s_beg + j + 2, lds0);
+                compute(lds1);
+            }
+        }
+    } else {
+        issue(s_beg, lds0);
+        if (nst > 1) issue(s_beg + 1, lds1);
+        for (int j = 0; j < nst; j += 3) {
+            sync_stage(j + 1 < nst);
+            if (j + 2 < nst) issue(s_beg + j + 2, lds2);
+            compute(lds0);
+            if (j + 1 >= nst) break;
+            sync_stage(j + 2 < nst);
+            if (j + 3 < nst) issue(s_beg + j + 3, lds0);
             compute(lds1);
+            if (j + 2 >= nst) break;
+            sync_stage(j + 3 < nst);
+            if (j + 4 < nst) issue(s_beg + j + 4, lds1);
+            compute(lds2);
         }
     }
 
@@ -309,12 +341,14 @@ __global__ __launch_bounds__(256) void k_split_epilogue(ApplyArgs a, const float
     const int cb0 = static_cast<int>(blockIdx.x) * 4;
     const f32x4_t *p = reinterpret_cast<const f32x4_t *>(part) + (static_cast<size_t>(rb) * ncb + cb0) * 64 + lane;
     const size_t zs = static_cast<size_t>(nrb) * ncb * 64;
+    // Every split's loads issued at once (split index clamped; repeats are
+    // not added), so the wait counts stay exact.
     f32x4_t v[MAX_TSPLIT][4];
 #pragma unroll
     for (int z = 0; z < MAX_TSPLIT; ++z)
-        if (z < splits)
 #pragma unroll
-            for (int wc = 0; wc < 4; ++wc) v[z][wc] = p[z * zs + wc * 64];
+        for (int wc = 0; wc < 4; ++wc) v[z][wc] = p[min(z, splits - 1) * zs + wc * 64];
+    asm volatile("" ::: "memory");
     f32x4_t acc[1][4];
 #pragma unroll
     for (int wc = 0; wc < 4; ++wc) {

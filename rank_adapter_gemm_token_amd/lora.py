@@ -42,6 +42,7 @@ TORCH_DTYPE = {v: k for k, v in DTYPE_OF.items()}
 # Every symbol include/lora.h declares, in declaration order.
 EXPORTS = ["lora_pool_create", "lora_pool_destroy", "lora_set_tenant_quota", "lora_register",
            "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_route",
+           "lora_plan_create", "lora_plan_destroy", "lora_plan_route", "lora_apply_routed",
            "lora_pool_stats", "lora_tenant_bytes", "lora_poll_errors", "lora_profile_enable",
            "lora_profile_read", "lora_strerror", "lora_last_hip_error"]
 
@@ -76,6 +77,10 @@ _lib.lora_set_policy.argtypes = [_vp, _i, _i]
 _lib.lora_get_policy.argtypes = [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i)]
 _lib.lora_apply.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
 _lib.lora_route.argtypes = [_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.lora_plan_create.argtypes = [_i, _i, ctypes.POINTER(_vp)]
+_lib.lora_plan_destroy.argtypes = [_vp]
+_lib.lora_plan_route.argtypes = [_vp, _vp, _vp, _i, _vp]
+_lib.lora_apply_routed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
 _lib.lora_pool_stats.argtypes = [_vp, ctypes.POINTER(lora_stats)]
 _lib.lora_tenant_bytes.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]
 _lib.lora_poll_errors.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
@@ -209,6 +214,44 @@ def lora_route(pool, token_adapter_idx, n_tokens, counts, offsets, perm, segs, n
         _need(n_seg, 1, torch.int32, "n_seg")
     _check(_lib.lora_route(pool, _ptr(token_adapter_idx), int(n_tokens), _ptr(counts), _ptr(offsets),
                            _ptr(perm), _ptr(segs), _ptr(n_seg), _stream(stream)), "lora_route")
+
+
+# Plans created through this binding: capacity and the last routed batch size.
+_plans = {}
+
+
+def lora_plan_create(max_tokens, n_slots):
+    """Returns the plan handle (an int)."""
+    h = _vp()
+    _check(_lib.lora_plan_create(int(max_tokens), int(n_slots), ctypes.byref(h)), "lora_plan_create")
+    _plans[h.value] = dict(max_T=max_tokens, S=n_slots, T=None)
+    return h.value
+
+
+def lora_plan_destroy(plan):
+    _check(_lib.lora_plan_destroy(plan), "lora_plan_destroy")
+    _plans.pop(plan, None)
+
+
+def lora_plan_route(plan, pool, token_adapter_idx, n_tokens, stream=None):
+    pl = _plans.get(plan)
+    if pl is not None and 0 <= n_tokens <= pl["max_T"]:
+        _need(token_adapter_idx, n_tokens, torch.int32, "token_adapter_idx")
+    _check(_lib.lora_plan_route(plan, pool, _ptr(token_adapter_idx), int(n_tokens), _stream(stream)),
+           "lora_plan_route")
+    if pl is not None:
+        pl["T"] = int(n_tokens)
+
+
+def lora_apply_routed(pool, plan, x, W_base, y, stream=None):
+    sh, pl = _shapes.get(pool), _plans.get(plan)
+    if sh is not None and pl is not None and pl["T"] is not None and 0 < pl["T"] <= sh["max_T"]:
+        T = pl["T"]
+        _need(x, T * sh["d_in"], sh["dtype"], "x")
+        _need(W_base, sh["d_out"] * sh["d_in"], sh["dtype"], "W_base")
+        _need(y, T * sh["d_out"], sh["dtype"], "y")
+    _check(_lib.lora_apply_routed(pool, plan, _ptr(x), _ptr(W_base), _ptr(y), _stream(stream)),
+           "lora_apply_routed")
 
 
 def lora_pool_stats(pool):

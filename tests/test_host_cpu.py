@@ -82,6 +82,14 @@ def test_validation_before_device_use():
     v = ctypes.c_uint64()
     assert lib.lora_poll_errors(None, ctypes.byref(v)) == L.LORA_EINVAL
     assert lib.lora_tenant_bytes(None, 0, ctypes.byref(v)) == L.LORA_EINVAL
+    # Plans: bad sizes and null handles are refused before the device.
+    assert lib.lora_plan_create(0, 4, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_plan_create(16, 0, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_plan_create(16, 1025, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_plan_create(16, 4, None) == L.LORA_EINVAL
+    assert lib.lora_plan_destroy(None) == L.LORA_OK
+    assert lib.lora_plan_route(None, None, None, 4, None) == L.LORA_EINVAL
+    assert lib.lora_apply_routed(None, None, None, None, None, None) == L.LORA_EINVAL
 
 
 def test_stats_struct_layout_matches_header(tmp_path):
