@@ -404,6 +404,15 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)
         log("cpu baseline:", cpu)
 
+    # The rank-padding share of the batch's LoRA rows (the shrink and expand
+    # skip those rank blocks), from one routed call's pool statistics.
+    c0 = steps[0][0]
+    L.lora_apply(c0.pool, c0.x, c0.W, c0.idx, c0.T, c0.y)
+    st = L.lora_pool_stats(c0.pool)
+    zero_pad = {"rows_padded": st["last_lora_rows_padded"], "rows_true": st["last_lora_rows_true"],
+                "fraction": st["last_zero_pad_fraction"]}
+    log("zero pad:", zero_pad)
+
     step_s = sec / args.steps
     out = {
         "metric": METRIC,
@@ -432,6 +441,7 @@ def main():
         "stage_us_per_call": None if stages is None else {k.replace("_ms", ""): v * 1e3
                                                           for k, v in stages.items()},
         "cpu_baseline": cpu,
+        "zero_pad": zero_pad,
     }
     print(json.dumps(out), flush=True)
 

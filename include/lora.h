@@ -231,8 +231,8 @@ int lora_plan_destroy(lora_plan plan);
  * table and fused/separate policy (p->n_slots must equal the plan's).  Copies
  * token_adapter_idx (device int32 [n_tokens]) into the plan, then runs the
  * routing kernel.  Invalid tokens are counted once, here, on p's error
- * counter.  The plan records p's active slots, policy and threshold at this
- * call; lora_apply_routed checks them.
+ * counter.  The plan records p's active slots with their ranks, policy and
+ * threshold at this call; lora_apply_routed checks them.
  * Errors: LORA_EINVAL, LORA_ETOKENS (n_tokens > the plan's max_tokens),
  * LORA_EMISMATCH (slot count differs), LORA_EHIP. */
 int lora_plan_route(lora_plan plan, lora_pool p, const int32_t *token_adapter_idx, int n_tokens,
@@ -242,10 +242,10 @@ int lora_plan_route(lora_plan plan, lora_pool p, const int32_t *token_adapter_id
  * routing pass: the plan's routing and token indices are used.  Must follow
  * the lora_plan_route on the same stream (or an event that orders them).
  * The result equals lora_apply's with the same indices bit for bit.  Pool p
- * must match the routing pool in slot count, active slots, policy and
- * threshold (as of the route call), else LORA_EMISMATCH and nothing is
- * enqueued: its adapters (A, B, scales) may differ -- one plan serves the
- * pools of every linear of a model.  Leaves p's last-call statistics and
+ * must match the routing pool in slot count, active slots and their ranks,
+ * policy and threshold (as of the route call), else LORA_EMISMATCH and
+ * nothing is enqueued: its adapters' values (A, B, alpha) may differ -- one
+ * plan serves the pools of every linear of a model.  Leaves p's last-call statistics and
  * error counter unchanged.
  * Errors (host-side, nothing enqueued): LORA_EINVAL (no routed batch,
  * pointers), LORA_ETOKENS, LORA_EMISMATCH, LORA_EHIP. */

@@ -114,7 +114,7 @@ struct lora_plan_s {
     // lora_plan_route).
     int T = -1;
     int policy = 0, theta = 0;
-    std::vector<uint8_t> active;  // [S] slot was ACTIVE
+    std::vector<int> rank;        // [S] the slot's rank if ACTIVE, else 0 (tiles carry ranks)
     hipEvent_t done = nullptr;    // after the routing was enqueued
     hipStream_t done_stream = nullptr;
 };
@@ -609,8 +609,9 @@ int lora_plan_route(lora_plan plan, lora_pool p, const int32_t *token_adapter_id
     plan->done_stream = st;
     plan->policy = p->policy;
     plan->theta = p->theta;
-    plan->active.assign(static_cast<size_t>(p->S), 0);
-    for (int i = 0; i < p->S; ++i) plan->active[i] = p->book.slot(i).state == lora::SlotState::Active ? 1 : 0;
+    plan->rank.assign(static_cast<size_t>(p->S), 0);
+    for (int i = 0; i < p->S; ++i)
+        if (p->book.slot(i).state == lora::SlotState::Active) plan->rank[i] = p->book.slot(i).rank;
     plan->T = n_tokens;
     return LORA_OK;
 }
@@ -627,11 +628,14 @@ int lora_apply_routed(lora_pool p, lora_plan plan, const void *x, const void *W_
 
     std::lock_guard<std::mutex> lk(p->mu);
     // The plan's routing holds for this pool only if every input of the
-    // routing matches: slot count, which slots are ACTIVE, policy, threshold.
+    // routing matches: slot count, which slots are ACTIVE and their ranks
+    // (the bucket tiles carry them), policy, threshold.
     if (p->S != plan->S || p->device != plan->device || p->policy != plan->policy || p->theta != plan->theta)
         return LORA_EMISMATCH;
-    for (int i = 0; i < p->S; ++i)
-        if ((p->book.slot(i).state == lora::SlotState::Active ? 1 : 0) != plan->active[i]) return LORA_EMISMATCH;
+    for (int i = 0; i < p->S; ++i) {
+        const lora::SlotRecord &rec = p->book.slot(i);
+        if ((rec.state == lora::SlotState::Active ? rec.rank : 0) != plan->rank[i]) return LORA_EMISMATCH;
+    }
     DeviceGuard g(p->device);
     HIP_TRY(g.error());
     return apply_locked(p, x, W_base, plan->idx, n_tokens, y, static_cast<hipStream_t>(stream), &plan->ro);

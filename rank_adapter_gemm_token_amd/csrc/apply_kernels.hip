@@ -68,7 +68,7 @@ __device__ __forceinline__ void finish(const ApplyArgs &a, int row, int col, flo
 __global__ __launch_bounds__(256) void k_shrink_f32(ApplyArgs a) {
     const int tile = blockIdx.x;
     if (tile >= *a.rv.n_tiles) return;
-    const int seg = a.rv.tiles[2 * tile];
+    const int seg = tile_seg(a.rv.tiles[2 * tile]);
     const int row0 = a.rv.tiles[2 * tile + 1];
     const int key = a.rv.segs[4 * seg];
     const int end = a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2];
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void k_expand_separate(ApplyArgs a) {
     using raw = typename E::raw;
     const int tile = blockIdx.x;
     if (tile >= *a.rv.n_tiles) return;
-    const int seg = a.rv.tiles[2 * tile];
+    const int seg = tile_seg(a.rv.tiles[2 * tile]);
     const int row0 = a.rv.tiles[2 * tile + 1];
     const int key = a.rv.segs[4 * seg];
     const int end = a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2];

@@ -29,15 +29,18 @@ __device__ __forceinline__ int token_of(const ApplyArgs &a, int p) {
 }
 
 // Partial h = x_tile . A_slot^T over k part `part` (of h_parts) for one
-// 16-row tile of an adapter bucket: slot `key`, sorted rows row0 .. row0 +
-// rows - 1, whose tokens are perm[row0 ..] (perm may live in LDS or global
-// memory).  One workgroup of NWV waves; the part's k steps are split over the
+// 16-row tile of an adapter bucket: slot `key` of true rank `rank`, sorted
+// rows row0 .. row0 + rows - 1, whose tokens are perm[row0 ..] (perm may
+// live in LDS or global memory).  RB rank blocks of 16 are computed: the
+// caller picks RB to cover the slot's true rank; h's columns past them (A
+// rows that are zero) are stored as exact zeros.  RB also sets how many k
+// steps a wave keeps in flight (U).  One workgroup of NWV waves; the part's k steps are split over the
 // waves and the waves' sums are added in LDS in a fixed order.  `lds` holds
 // >= NWV * RB * 64 16-byte words.  The part is written to h + part * T * R;
 // consumers add the parts in order.
 template <int DT, int RB, int NWV>
-__device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row0, int rows, const int32_t *perm,
-                                            int part, u32x4_t *lds) {
+__device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row0, int rows,
+                                            const int32_t *perm, int part, u32x4_t *lds) {
     using E = Elem<DT>;
     using V = typename E::vec8;
     key = uniform(key);
@@ -107,17 +110,31 @@ __device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row
             if (row < rows && j < Rp) hout[static_cast<size_t>(row0 + row) * Rp + j] = s[i];
         }
     }
+    for (int j = RB * 16 + r; j < Rp; j += 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = kq * 4 + i;
+            if (row < rows) hout[static_cast<size_t>(row0 + row) * Rp + j] = 0.0f;
+        }
+    }
 }
 
 // shrink_unit for tile `tile` of the routing in global memory.
 template <int DT, int RB, int NWV>
 __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int part, u32x4_t *lds) {
     if (tile >= uniform(*a.rv.n_tiles)) return;
-    const int seg = a.rv.tiles[2 * tile];
+    const int tw = a.rv.tiles[2 * tile];
+    const int seg = tile_seg(tw);
     const int row0 = a.rv.tiles[2 * tile + 1];
     const int key = a.rv.segs[4 * seg];
     const int end = a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2];
-    shrink_unit<DT, RB, NWV>(a, key, row0, min(TILE_ROWS, end - row0), a.rv.perm, part, lds);
+    const int rows = min(TILE_ROWS, end - row0);
+    // Rank blocks that hold the slot's true rank (the tile carries it).
+    const int nrb = uniform(min(RB, (tile_rank(tw) + 15) / 16));
+    if (RB >= 4 && nrb == 4) shrink_unit<DT, (RB >= 4 ? 4 : 1), NWV>(a, key, row0, rows, a.rv.perm, part, lds);
+    else if (RB >= 3 && nrb == 3) shrink_unit<DT, (RB >= 3 ? 3 : 1), NWV>(a, key, row0, rows, a.rv.perm, part, lds);
+    else if (RB >= 2 && nrb == 2) shrink_unit<DT, (RB >= 2 ? 2 : 1), NWV>(a, key, row0, rows, a.rv.perm, part, lds);
+    else shrink_unit<DT, 1, NWV>(a, key, row0, rows, a.rv.perm, part, lds);
 }
 
 // h[p][j .. j+7] summed over the shrink's k parts in order (p: the h row,
@@ -164,6 +181,7 @@ struct RowFacts {
     int tok[TB];
     int key[TB];
     int mode[TB];
+    int rank[TB];  // the slot's true rank (rank steps past it are skipped)
     float s[TB];
 };
 
@@ -182,7 +200,11 @@ __device__ __forceinline__ void row_facts(const ApplyArgs &a, int p0, int rows_e
         f.mode[tb] = a.rv.segs[4 * f.g[tb] + 3];
     }
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) f.s[tb] = a.slots[min(f.key[tb], a.S - 1)].scale;
+    for (int tb = 0; tb < TB; ++tb) {
+        const SlotDev *sd = a.slots + min(f.key[tb], a.S - 1);
+        f.s[tb] = sd->scale;
+        f.rank[tb] = sd->rank;
+    }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
         if (p0 + tb * 16 + r >= rows_end) f.g[tb] = -1;
@@ -249,9 +271,11 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
     for (int tb = 0; tb < TB; ++tb) other = other || (f.g[tb] >= 0 && f.g[tb] != g_first);
     if (__ballot(other) == 0) {
         const int key = uniform(f.key[0]);
+        // Rank steps holding the true rank (B columns past it are zero).
+        const int njs = uniform(min((Rp + 31) / 32, (f.rank[0] + 31) / 32));
 #pragma unroll
         for (int js = 0; js < JM; ++js) {
-            if (js * 32 >= Rp) break;
+            if (js >= njs) break;
             V bf[WC];
             load_b(key, js, bf);
             float hv[2][8];
@@ -285,10 +309,11 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
             const int l0 = __ffsll(static_cast<long long>(m)) - 1;
             const int key = __builtin_amdgcn_readlane(f.key[tb], l0);
             const int mode = __builtin_amdgcn_readlane(f.mode[tb], l0);
+            const int rk = __builtin_amdgcn_readlane(f.rank[tb], l0);
             if (key >= a.S || mode != want) continue;
 #pragma unroll
             for (int js = 0; js < JM; ++js) {
-                if (js * 32 >= Rp) break;
+                if (js * 32 >= Rp || js * 32 >= rk) break;
                 V bf[WC];
                 load_b(key, js, bf);
                 const V h = make_h(tb, js, gg, hv[js]);

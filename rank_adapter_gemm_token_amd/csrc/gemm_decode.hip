@@ -72,7 +72,7 @@ struct SmallRoute {
     alignas(16) int key[DECODE_MAX_T];  // token -> key (lanes >= T: past every key)
     int rank[DECODE_MAX_T];     // token -> true rank (LoRA tokens)
     int segs[SMAX_SEG][4];      // {key, start, len, mode}
-    int tiles[DECODE_MAX_T + SMAX_SEG][2];  // {bucket, first row}
+    int tiles[DECODE_MAX_T + SMAX_SEG][2];  // {bucket | rank << 16 (tile_pack), first row}
     int n_seg;
     int n_lora;                 // LoRA buckets (records 0 .. n_lora-1)
     int n_tiles;
@@ -156,7 +156,7 @@ __device__ __forceinline__ void small_route(int v, int state, int rank_in, int T
         sr.segs[seg][2] = len;
         sr.segs[seg][3] = mode;
         for (int j = 0; j < nt; ++j) {
-            sr.tiles[tile0 + j][0] = seg;
+            sr.tiles[tile0 + j][0] = tile_pack(seg, sr.rank[ptok]);
             sr.tiles[tile0 + j][1] = p + j * TILE_ROWS;
         }
     }

@@ -150,6 +150,24 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
 // k_split_epilogue adds them.
 using lds_ptr = __attribute__((address_space(3))) void *;
 
+// Output tile of workgroup `id` (of nx x ny): workgroups are dealt to the 8
+// XCDs round-robin (id mod 8), so XCD k takes the k-th eighth of a grouped
+// order -- 4 row tiles at a time, column by column -- and its workgroups share
+// x rows and W columns in that XCD's L2 instead of each XCD fetching most of
+// both.  A bijection for any nx, ny (without the XCD split when 8 does not
+// divide the tile count).
+__device__ __forceinline__ void xcd_tile_order(int nx, int ny, int id, int &tm, int &tn) {
+    constexpr int G = 4;
+    const int n = nx * ny;
+    const int ord = (n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id;
+    const int group = ord / (G * nx);
+    const int first = group * G;
+    const int rows = min(G, ny - first);
+    const int r = ord - first * nx;
+    tm = first + r % rows;
+    tn = r / rows;
+}
+
 template <int DT, int BN, bool SPLIT>
 __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     using E = Elem<DT>;
@@ -172,8 +190,10 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     const int g = lane >> 4;
     const int wm = wave >> 2;  // rows wm * 128
     const int wn = wave & 3;   // columns wn * BN / 4
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
+    int tm = blockIdx.y, tn = blockIdx.x;
+    if (!SPLIT) xcd_tile_order(gridDim.x, gridDim.y, blockIdx.x + gridDim.x * blockIdx.y, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
     const int nst_all = a.d_in / 64;
     const int s_beg = SPLIT ? uniform(static_cast<int>(blockIdx.z) * nst_all / static_cast<int>(gridDim.z)) : 0;
     const int s_end = SPLIT ? uniform((static_cast<int>(blockIdx.z) + 1) * nst_all / static_cast<int>(gridDim.z))

@@ -65,6 +65,13 @@ struct RouteView {
 };
 
 // Upper bound of the number of LoRA-bucket tiles of a T-token call.
+// A bucket tile's first word: its bucket record in the low 16 bits, the
+// slot's true rank above them (shrink and expand skip the rank blocks past
+// it: those A rows and B columns are zero).
+__host__ __device__ inline int tile_pack(int seg, int rank) { return seg | (rank << 16); }
+__host__ __device__ inline int tile_seg(int v) { return v & 0xFFFF; }
+__host__ __device__ inline int tile_rank(int v) { return v >> 16; }
+
 inline int max_tiles(int T, int S) {
     return (T + TILE_ROWS - 1) / TILE_ROWS + (S < T ? S : T);
 }

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
                 if (out.tiles != nullptr) {
                     const int nt = (n + TILE_ROWS - 1) / TILE_ROWS;
                     for (int j = 0; j < nt; ++j) {
-                        out.tiles[2 * (s_tile[k] + j)] = s_seg[k];
+                        out.tiles[2 * (s_tile[k] + j)] = tile_pack(s_seg[k], slots[k].rank);
                         out.tiles[2 * (s_tile[k] + j) + 1] = s_off[k] + j * TILE_ROWS;
                     }
                 }

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void k_expand_sep(ApplyArgs a) {
     using raw = typename E::raw;
     const int tile = blockIdx.x;
     if (tile >= uniform(*a.rv.n_tiles)) return;
-    const int seg = uniform(a.rv.tiles[2 * tile]);
+    const int seg = uniform(tile_seg(a.rv.tiles[2 * tile]));
     if (uniform(a.rv.segs[4 * seg + 3]) != SEG_SEPARATE) return;
     const int row0 = uniform(a.rv.tiles[2 * tile + 1]);
     const int end = uniform(a.rv.segs[4 * seg + 1] + a.rv.segs[4 * seg + 2]);

@@ -3,8 +3,9 @@ through the C ABI.
 
 A routed apply runs the same kernels on the same routing as lora_apply, so
 its output must equal lora_apply's bit for bit -- on the routing pool and on
-any other pool with the same slot count, active slots and policy (other
-adapters, other weights): one plan serves every linear of a step.  A pool
+any other pool with the same slot count, active slots, ranks and policy
+(other adapter values, other weights): one plan serves every linear of a
+step.  A pool
 whose routing inputs differ is refused (LORA_EMISMATCH) before anything is
 enqueued.  lora_apply itself is compared with the oracle elsewhere
 (test_apply_gpu.py)."""
@@ -14,16 +15,30 @@ import torch
 
 from gpu_helpers import Pool, assert_close, dev, reference
 from rank_adapter_gemm_token_amd import lora
+from rank_adapter_gemm_token_amd import workloads as wl
 from test_apply_gpu import _small_case
 
 pytestmark = pytest.mark.gpu
 
 
-def _pool_with(dtype, T, d_in, d_out, S, R, seed, policy=0):
+def _pool_with(dtype, T, d_in, d_out, S, R, seed, policy=0, ranks=None):
+    """A pool of S adapters; `ranks` (slot -> rank) fixes the ranks (the
+    adapters' values still come from `seed`)."""
     x, W, ads, idx = _small_case(dtype, T, d_in, d_out, S, R, seed)
+    if ranks is not None:
+        rng = np.random.default_rng(seed + 1000)
+        tdt = x.dtype
+        ads = [wl.Adapter(a.slot, a.tenant, ranks[a.slot], float(2 * ranks[a.slot]),
+                          torch.from_numpy(rng.standard_normal((ranks[a.slot], d_in)) / np.sqrt(d_in)).to(tdt),
+                          torch.from_numpy(rng.standard_normal((d_out, ranks[a.slot])) * 0.1).to(tdt))
+               for a in ads]
     p = Pool(d_in, d_out, R, S, T, dtype, policy, 4)
     p.register_all(ads)
     return p, x, W, idx
+
+
+def _ranks(p):
+    return {s: v[2] for s, v in p.adapters.items()}
 
 
 def _routed(p, plan, x, W, T):
@@ -40,8 +55,9 @@ def _routed(p, plan, x, W, T):
 @pytest.mark.parametrize("policy", [0, 2])
 def test_routed_equals_apply_across_pools(dtype, T, d_in, d_out, S, R, policy):
     pa, xa, Wa, idx = _pool_with(dtype, T, d_in, d_out, S, R, seed=T + 1, policy=policy)
-    # A second linear: same slot count and active set, other adapters and W.
-    pb, xb, Wb, _ = _pool_with(dtype, T, d_in, d_out, S, R, seed=T + 2, policy=policy)
+    # A second linear: same slot count, active slots and ranks; other adapter
+    # values and W.
+    pb, xb, Wb, _ = _pool_with(dtype, T, d_in, d_out, S, R, seed=T + 2, policy=policy, ranks=_ranks(pa))
     plan = lora.lora_plan_create(T, S)
     try:
         ya = pa.apply(dev(xa), dev(Wa), dev(idx))
@@ -66,7 +82,7 @@ def test_routed_equals_apply_across_pools(dtype, T, d_in, d_out, S, R, policy):
 def test_plan_reused_for_many_calls_and_errors_counted_once():
     T, S = 130, 9
     pa, xa, Wa, idx = _pool_with("bf16", T, 256, 128, S, 16, seed=5)
-    pb, xb, Wb, _ = _pool_with("bf16", T, 256, 128, S, 16, seed=6)
+    pb, xb, Wb, _ = _pool_with("bf16", T, 256, 128, S, 16, seed=6, ranks=_ranks(pa))
     n_inv = int(((idx < -1) | (idx >= S)).sum())
     assert n_inv > 0
     plan = lora.lora_plan_create(T + 10, S)
@@ -95,17 +111,23 @@ def test_mismatched_pools_are_refused():
     others = []
     try:
         lora.lora_plan_route(plan, pa.h, dev(idx), T)
+        rk = _ranks(pa)
         # Fewer active slots.
-        pc, xc, Wc, _ = _pool_with("f16", T, 128, 128, S, 8, seed=12)
+        pc, xc, Wc, _ = _pool_with("f16", T, 128, 128, S, 8, seed=12, ranks=rk)
         others.append(pc)
         pc.unregister(3)
         # Other policy.
-        pd, xd, Wd, _ = _pool_with("f16", T, 128, 128, S, 8, seed=13, policy=2)
+        pd, xd, Wd, _ = _pool_with("f16", T, 128, 128, S, 8, seed=13, policy=2, ranks=rk)
         others.append(pd)
         # Other slot count (routing into it is refused too).
         pe, xe, We, _ = _pool_with("f16", T, 128, 128, S + 1, 8, seed=14)
         others.append(pe)
-        for p, x, W in ((pc, xc, Wc), (pd, xd, Wd), (pe, xe, We)):
+        # Same active slots, one of another rank.
+        rk2 = dict(rk)
+        rk2[2] = 1 if rk[2] != 1 else 2
+        pf, xf, Wf, _ = _pool_with("f16", T, 128, 128, S, 8, seed=15, ranks=rk2)
+        others.append(pf)
+        for p, x, W in ((pc, xc, Wc), (pd, xd, Wd), (pe, xe, We), (pf, xf, Wf)):
             y = torch.full((T, p.d_out), 3.0, dtype=torch.float16, device="cuda")
             with pytest.raises(lora.LoraError) as ei:
                 lora.lora_apply_routed(p.h, plan, dev(x), dev(W), y)
