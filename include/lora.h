@@ -62,6 +62,7 @@ extern "C" {
 
 typedef struct lora_pool_s *lora_pool; /* opaque; owned by the library */
 typedef struct lora_plan_s *lora_plan; /* opaque routing plan; owned by the library */
+typedef struct lora_loader_s *lora_loader; /* opaque host-to-slot loader; owned by the library */
 
 typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
 
@@ -251,6 +252,47 @@ int lora_plan_route(lora_plan plan, lora_pool p, const int32_t *token_adapter_id
  * pointers), LORA_ETOKENS, LORA_EMISMATCH, LORA_EHIP. */
 int lora_apply_routed(lora_pool p, lora_plan plan, const void *x, const void *W_base, void *y,
                       void *stream);
+
+/* ------------------------------------------------------- async loading -- */
+
+/* The adapter loader ["LLM 多 LoRA 推理服务工程 2026", four-layer runtime,
+ * loader paragraph]: moves an adapter from host memory into a pool slot
+ * without blocking the hot path -- two pinned host staging buffers and two
+ * device staging buffers (double buffering: one copy in flight while the
+ * next adapter is staged), a copy stream of its own, and the register-time
+ * pad kernel on that stream.  One loader serves any pools of its device.
+ * capacity_bytes bounds one adapter's A and B together
+ * (rank * (d_in + d_out) * element size).  Allocates once, here.
+ * Errors: LORA_EINVAL (capacity 0, out == NULL), LORA_ENOMEM, LORA_EHIP. */
+int lora_loader_create(uint64_t capacity_bytes, lora_loader *out);
+
+/* Waits for and commits every pending load, then frees the loader. */
+int lora_loader_destroy(lora_loader l);
+
+/* Start loading an adapter into `slot` of pool p from host memory:
+ *   A_host  [rank][d_in], B_host [d_out][rank], the pool's dtype, any host
+ *           memory (copied into pinned staging before this call returns; the
+ *           caller may reuse it at once)
+ * The slot is reserved against the tenant's quota at once (the same checks
+ * and errors as lora_register, nothing changes on error) and stays LOADING
+ * -- tokens naming it are invalid -- until the load is committed by
+ * lora_load_poll / lora_load_wait (or by a later load reusing its staging
+ * buffer), which makes it ACTIVE.  When both staging buffers are in flight
+ * the call first waits for the older one.  *ticket identifies the load.
+ * The caller must wait for its loads before destroying the pool.
+ * Errors: LORA_EINVAL (NULL pointers, slot out of range, adapter larger than
+ * the loader's capacity), LORA_ESLOT_BUSY, LORA_ERANK, LORA_EALPHA,
+ * LORA_EQUOTA, LORA_EHIP. */
+int lora_load_async(lora_loader l, lora_pool p, int slot, int32_t tenant, const void *A_host,
+                    const void *B_host, int rank, float alpha, uint64_t *ticket);
+
+/* Non-blocking: *done = 1 (and the slot committed, ACTIVE) once the load's
+ * copies finished, else 0.  Errors: LORA_EINVAL (unknown ticket), LORA_EHIP. */
+int lora_load_poll(lora_loader l, uint64_t ticket, int *done);
+
+/* Blocking: wait for the load's copies, then commit it.  A ticket that was
+ * committed already returns LORA_OK.  Errors: LORA_EINVAL, LORA_EHIP. */
+int lora_load_wait(lora_loader l, uint64_t ticket);
 
 /* ---------------------------------------------------------- observation -- */
 

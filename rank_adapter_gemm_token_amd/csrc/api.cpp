@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <new>
 #include <string>
@@ -117,6 +118,27 @@ struct lora_plan_s {
     std::vector<int> rank;        // [S] the slot's rank if ACTIVE, else 0 (tiles carry ranks)
     hipEvent_t done = nullptr;    // after the routing was enqueued
     hipStream_t done_stream = nullptr;
+};
+
+struct lora_loader_s {
+    int device = 0;
+    uint64_t cap = 0;              // bytes of A + B one staging buffer holds
+    hipStream_t copy = nullptr;    // the loader's copy stream
+    void *host[2] = {nullptr, nullptr};  // pinned staging
+    void *dev[2] = {nullptr, nullptr};   // device staging
+    hipEvent_t done[2] = {nullptr, nullptr};
+    uint64_t owner[2] = {0, 0};    // ticket whose copies a buffer holds (0: none pending)
+    int next = 0;
+    struct Pending {
+        lora_pool pool;
+        int slot;
+        int rank;
+        float alpha;
+        int buf;
+    };
+    std::map<uint64_t, Pending> pending;
+    uint64_t last_ticket = 0;
+    std::mutex mu;
 };
 
 namespace {
@@ -639,6 +661,175 @@ int lora_apply_routed(lora_pool p, lora_plan plan, const void *x, const void *W_
     DeviceGuard g(p->device);
     HIP_TRY(g.error());
     return apply_locked(p, x, W_base, plan->idx, n_tokens, y, static_cast<hipStream_t>(stream), &plan->ro);
+}
+
+int lora_loader_create(uint64_t capacity_bytes, lora_loader *out) {
+    if (out == nullptr) return LORA_EINVAL;
+    *out = nullptr;
+    if (capacity_bytes == 0) return LORA_EINVAL;
+    lora_loader l = new (std::nothrow) lora_loader_s;
+    if (l == nullptr) return LORA_ENOMEM;
+    l->cap = capacity_bytes;
+    hipError_t e = hipGetDevice(&l->device);
+    // Staging: A, then B at the next 256-byte boundary.
+    const size_t bytes = align_up(static_cast<size_t>(capacity_bytes), 256) + 256;
+    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+        e = hipHostMalloc(&l->host[b], bytes, hipHostMallocDefault);
+        if (e == hipSuccess) e = hipMalloc(&l->dev[b], bytes);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&l->done[b], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&l->copy, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+        const int rc = (e == hipErrorOutOfMemory) ? LORA_ENOMEM : hip_fail(e);
+        lora_loader_destroy(l);
+        return rc;
+    }
+    *out = l;
+    return LORA_OK;
+}
+
+namespace {
+
+// Make a finished load's slot ACTIVE: write its device slot entry, then the
+// host state (pool mutex taken here).  The loader's mutex is held.
+int commit_load(lora_loader l, uint64_t ticket) {
+    auto it = l->pending.find(ticket);
+    if (it == l->pending.end()) return LORA_OK;  // committed already
+    const lora_loader_s::Pending pd = it->second;
+    l->pending.erase(it);
+    if (l->owner[pd.buf] == ticket) l->owner[pd.buf] = 0;
+    lora_pool p = pd.pool;
+    std::lock_guard<std::mutex> lk(p->mu);
+    DeviceGuard g(p->device);
+    hipError_t e = g.error();
+    lora::SlotDev ent{lora::SLOT_ACTIVE, pd.rank, pd.alpha / static_cast<float>(pd.rank), 0};
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(p->slots_dev + pd.slot, &ent, sizeof ent, hipMemcpyHostToDevice, p->internal);
+    if (e == hipSuccess) e = hipStreamSynchronize(p->internal);
+    if (e != hipSuccess) {
+        p->book.abort_register(pd.slot);
+        return hip_fail(e);
+    }
+    p->book.commit_register(pd.slot);
+    return LORA_OK;
+}
+
+// Wait for staging buffer b's copies and commit the load that owns it.
+int retire_buffer(lora_loader l, int b) {
+    const uint64_t t = l->owner[b];
+    if (t == 0) return LORA_OK;
+    const hipError_t e = hipEventSynchronize(l->done[b]);
+    if (e != hipSuccess) return hip_fail(e);
+    return commit_load(l, t);
+}
+
+}  // namespace
+
+int lora_loader_destroy(lora_loader l) {
+    if (l == nullptr) return LORA_OK;
+    int rc = LORA_OK;
+    {
+        std::lock_guard<std::mutex> lk(l->mu);
+        DeviceGuard g(l->device);
+        for (int b = 0; b < 2; ++b) {
+            const int r = retire_buffer(l, b);
+            if (r != LORA_OK && rc == LORA_OK) rc = r;
+        }
+        for (int b = 0; b < 2; ++b) {
+            if (l->done[b]) (void)hipEventDestroy(l->done[b]);
+            if (l->dev[b]) (void)hipFree(l->dev[b]);
+            if (l->host[b]) (void)hipHostFree(l->host[b]);
+        }
+        if (l->copy) (void)hipStreamDestroy(l->copy);
+    }
+    delete l;
+    return rc;
+}
+
+int lora_load_async(lora_loader l, lora_pool p, int slot, int32_t tenant, const void *A_host, const void *B_host,
+                    int rank, float alpha, uint64_t *ticket) {
+    if (l == nullptr || p == nullptr || A_host == nullptr || B_host == nullptr || ticket == nullptr)
+        return LORA_EINVAL;
+    if (p->device != l->device) return LORA_EINVAL;
+    if (rank >= 1 && rank <= p->R) {
+        const uint64_t need = static_cast<uint64_t>(rank) * (p->d_in + p->d_out) * p->esz;
+        if (need > l->cap) return LORA_EINVAL;
+    }
+    std::lock_guard<std::mutex> lk(l->mu);
+    DeviceGuard g(l->device);
+    HIP_TRY(g.error());
+    // Take the older staging buffer; if its copies are still in flight, wait
+    // for them (and commit that load) first.
+    const int b = l->next;
+    const int rr = retire_buffer(l, b);
+    if (rr != LORA_OK) return rr;
+    {
+        std::lock_guard<std::mutex> pk(p->mu);
+        const int rc = p->book.begin_register(slot, tenant, rank, alpha);  // reserve: slot LOADING
+        if (rc != LORA_OK) return rc;
+    }
+    const size_t a_bytes = static_cast<size_t>(rank) * p->d_in * p->esz;
+    const size_t b_bytes = static_cast<size_t>(p->d_out) * rank * p->esz;
+    const size_t b_off = align_up(a_bytes, 256);
+    char *hs = static_cast<char *>(l->host[b]);
+    char *ds = static_cast<char *>(l->dev[b]);
+    std::memcpy(hs, A_host, a_bytes);
+    std::memcpy(hs + b_off, B_host, b_bytes);
+    hipError_t e = hipMemcpyAsync(ds, hs, b_off + b_bytes, hipMemcpyHostToDevice, l->copy);
+    if (e == hipSuccess)
+        e = lora::launch_pad_copy(ds, ds + b_off, p->A_slab, p->B_slab, slot, rank, p->Rp, p->d_in, p->d_out, p->esz,
+                                  l->copy);
+    if (e == hipSuccess) e = hipEventRecord(l->done[b], l->copy);
+    if (e == hipSuccess) {
+        std::lock_guard<std::mutex> pk(p->mu);
+        e = record_inflight(p, l->copy);  // unregister / destroy drain these copies
+    }
+    if (e != hipSuccess) {
+        std::lock_guard<std::mutex> pk(p->mu);
+        p->book.abort_register(slot);
+        return hip_fail(e);
+    }
+    const uint64_t t = ++l->last_ticket;
+    l->pending[t] = lora_loader_s::Pending{p, slot, rank, alpha, b};
+    l->owner[b] = t;
+    l->next = b ^ 1;
+    *ticket = t;
+    return LORA_OK;
+}
+
+int lora_load_poll(lora_loader l, uint64_t ticket, int *done) {
+    if (l == nullptr || done == nullptr) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(l->mu);
+    if (ticket == 0 || ticket > l->last_ticket) return LORA_EINVAL;
+    auto it = l->pending.find(ticket);
+    if (it == l->pending.end()) {
+        *done = 1;
+        return LORA_OK;
+    }
+    DeviceGuard g(l->device);
+    HIP_TRY(g.error());
+    const hipError_t e = hipEventQuery(l->done[it->second.buf]);
+    if (e == hipErrorNotReady) {
+        *done = 0;
+        return LORA_OK;
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    const int rc = commit_load(l, ticket);
+    *done = (rc == LORA_OK) ? 1 : 0;
+    return rc;
+}
+
+int lora_load_wait(lora_loader l, uint64_t ticket) {
+    if (l == nullptr) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(l->mu);
+    if (ticket == 0 || ticket > l->last_ticket) return LORA_EINVAL;
+    auto it = l->pending.find(ticket);
+    if (it == l->pending.end()) return LORA_OK;
+    DeviceGuard g(l->device);
+    HIP_TRY(g.error());
+    const hipError_t e = hipEventSynchronize(l->done[it->second.buf]);
+    if (e != hipSuccess) return hip_fail(e);
+    return commit_load(l, ticket);
 }
 
 int lora_pool_stats(lora_pool p, lora_stats *out) {

@@ -43,6 +43,7 @@ TORCH_DTYPE = {v: k for k, v in DTYPE_OF.items()}
 EXPORTS = ["lora_pool_create", "lora_pool_destroy", "lora_set_tenant_quota", "lora_register",
            "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_route",
            "lora_plan_create", "lora_plan_destroy", "lora_plan_route", "lora_apply_routed",
+           "lora_loader_create", "lora_loader_destroy", "lora_load_async", "lora_load_poll", "lora_load_wait",
            "lora_pool_stats", "lora_tenant_bytes", "lora_poll_errors", "lora_profile_enable",
            "lora_profile_read", "lora_strerror", "lora_last_hip_error"]
 
@@ -81,6 +82,12 @@ _lib.lora_plan_create.argtypes = [_i, _i, ctypes.POINTER(_vp)]
 _lib.lora_plan_destroy.argtypes = [_vp]
 _lib.lora_plan_route.argtypes = [_vp, _vp, _vp, _i, _vp]
 _lib.lora_apply_routed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
+_lib.lora_loader_create.argtypes = [ctypes.c_uint64, ctypes.POINTER(_vp)]
+_lib.lora_loader_destroy.argtypes = [_vp]
+_lib.lora_load_async.argtypes = [_vp, _vp, _i, ctypes.c_int32, _vp, _vp, _i, ctypes.c_float,
+                                 ctypes.POINTER(ctypes.c_uint64)]
+_lib.lora_load_poll.argtypes = [_vp, ctypes.c_uint64, ctypes.POINTER(_i)]
+_lib.lora_load_wait.argtypes = [_vp, ctypes.c_uint64]
 _lib.lora_pool_stats.argtypes = [_vp, ctypes.POINTER(lora_stats)]
 _lib.lora_tenant_bytes.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]
 _lib.lora_poll_errors.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
@@ -252,6 +259,50 @@ def lora_apply_routed(pool, plan, x, W_base, y, stream=None):
         _need(y, T * sh["d_out"], sh["dtype"], "y")
     _check(_lib.lora_apply_routed(pool, plan, _ptr(x), _ptr(W_base), _ptr(y), _stream(stream)),
            "lora_apply_routed")
+
+
+def lora_loader_create(capacity_bytes):
+    """Returns the loader handle (an int)."""
+    h = _vp()
+    _check(_lib.lora_loader_create(int(capacity_bytes), ctypes.byref(h)), "lora_loader_create")
+    return h.value
+
+
+def lora_loader_destroy(loader):
+    _check(_lib.lora_loader_destroy(loader), "lora_loader_destroy")
+
+
+def _host_ptr(t):
+    """Host pointer of a contiguous CPU tensor (or a raw int)."""
+    if isinstance(t, int):
+        return t
+    if t.is_cuda:
+        raise ValueError("expected a host tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def lora_load_async(loader, pool, slot, tenant, A_host, B_host, rank, alpha):
+    """Start loading host A [rank][d_in], B [d_out][rank] into `slot`; returns the ticket."""
+    sh = _shapes.get(pool)
+    if sh is not None and 0 < rank:
+        _need(A_host, rank * sh["d_in"], sh["dtype"], "A")
+        _need(B_host, sh["d_out"] * rank, sh["dtype"], "B")
+    t = ctypes.c_uint64()
+    _check(_lib.lora_load_async(loader, pool, int(slot), int(tenant), _host_ptr(A_host), _host_ptr(B_host),
+                                int(rank), float(alpha), ctypes.byref(t)), "lora_load_async")
+    return t.value
+
+
+def lora_load_poll(loader, ticket):
+    d = _i()
+    _check(_lib.lora_load_poll(loader, int(ticket), ctypes.byref(d)), "lora_load_poll")
+    return bool(d.value)
+
+
+def lora_load_wait(loader, ticket):
+    _check(_lib.lora_load_wait(loader, int(ticket)), "lora_load_wait")
 
 
 def lora_pool_stats(pool):

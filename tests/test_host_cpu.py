@@ -90,6 +90,15 @@ def test_validation_before_device_use():
     assert lib.lora_plan_destroy(None) == L.LORA_OK
     assert lib.lora_plan_route(None, None, None, 4, None) == L.LORA_EINVAL
     assert lib.lora_apply_routed(None, None, None, None, None, None) == L.LORA_EINVAL
+    # Loader: zero capacity, null handles.
+    assert lib.lora_loader_create(0, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_loader_create(1024, None) == L.LORA_EINVAL
+    assert lib.lora_loader_destroy(None) == L.LORA_OK
+    t = ctypes.c_uint64()
+    assert lib.lora_load_async(None, None, 0, 0, None, None, 8, ctypes.c_float(16.0), ctypes.byref(t)) == L.LORA_EINVAL
+    d = ctypes.c_int()
+    assert lib.lora_load_poll(None, 1, ctypes.byref(d)) == L.LORA_EINVAL
+    assert lib.lora_load_wait(None, 1) == L.LORA_EINVAL
 
 
 def test_stats_struct_layout_matches_header(tmp_path):
