@@ -272,6 +272,81 @@ def cpu_baseline(w, seconds):
 
 # ----------------------------------------------------------------------------
 
+def loader_bench(L, args):
+    """Adapter load latency through the async loader (lora_load_async): a
+    whole-model adapter (rank 16 on the 224 linears of the 7B stack, bf16,
+    from ordinary host memory) switched into every linear's pool, and the
+    per-linear load latency (async + wait) distribution.  One JSON line."""
+    import time
+    from rank_adapter_gemm_token_amd import workloads as wl
+    r = 16
+    rng = np.random.default_rng(7)
+    lins = []
+    for layer in range(wl.STACK_LAYERS):
+        for name, d_in, d_out in wl.STACK_SHAPES:
+            A = torch.from_numpy(rng.standard_normal((r, d_in), dtype=np.float32) / np.sqrt(d_in)).to(torch.bfloat16)
+            B = torch.from_numpy(rng.standard_normal((d_out, r), dtype=np.float32) * 0.1).to(torch.bfloat16)
+            lins.append((d_in, d_out, A.contiguous(), B.contiguous()))
+    pools = []
+    for d_in, d_out, _, _ in lins:
+        p = L.lora_pool_create(d_in, d_out, r, 2, 1, torch.bfloat16)
+        L.lora_set_tenant_quota(p, 0, 1 << 40)
+        pools.append(p)
+    cap = max(r * (d_in + d_out) * 2 for d_in, d_out, _, _ in lins)
+    ld = L.lora_loader_create(cap)
+    total_bytes = sum(r * (d_in + d_out) * 2 for d_in, d_out, _, _ in lins)
+
+    def switch(slot):
+        # Unload what the slot held, then load the whole adapter into it.
+        for p in pools:
+            try:
+                L.lora_unregister(p, slot)
+            except L.LoraError:
+                pass
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tickets = [L.lora_load_async(ld, p, slot, 0, A, B, r, 2.0 * r) for p, (_, _, A, B) in zip(pools, lins)]
+        for t in tickets:
+            L.lora_load_wait(ld, t)
+        return time.perf_counter() - t0
+
+    switch(0)  # warm-up
+    whole = [switch(k % 2) for k in range(args.loader_rounds)]
+    per = []
+    for k in range(2):
+        for p, (_, _, A, B) in zip(pools, lins):
+            L.lora_unregister(p, k)
+            t0 = time.perf_counter()
+            t = L.lora_load_async(ld, p, k, 0, A, B, r, 2.0 * r)
+            L.lora_load_wait(ld, t)
+            per.append(time.perf_counter() - t0)
+    # Plain pinned host -> device copy of the same byte count (the link's rate).
+    src = torch.empty(total_bytes, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(total_bytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d = total_bytes * 5 / (time.perf_counter() - t0) / 1e9
+    L.lora_loader_destroy(ld)
+    for p in pools:
+        L.lora_pool_destroy(p)
+    whole_ms = sorted(1e3 * v for v in whole)
+    per_ms = sorted(1e3 * v for v in per)
+    pct = lambda v, q: v[min(len(v) - 1, int(q * len(v)))]
+    out = {"loader": "whole-model adapter switch (rank 16 on 224 linears of the 7B stack, bf16) and "
+                     "per-linear loads, host memory -> pool slot via lora_load_async",
+           "adapter_bytes": total_bytes, "linears": len(lins), "rounds": len(whole),
+           "switch_ms": {"p50": pct(whole_ms, 0.5), "p95": pct(whole_ms, 0.95), "max": whole_ms[-1]},
+           "switch_GBs": total_bytes / (whole_ms[len(whole_ms) // 2] / 1e3) / 1e9,
+           "per_linear_ms": {"p50": pct(per_ms, 0.5), "p95": pct(per_ms, 0.95), "max": per_ms[-1],
+                             "n": len(per_ms)},
+           "pinned_h2d_copy_GBs": h2d}
+    print(json.dumps(out), flush=True)
+
+
 def theta_sweep(L, args):
     """The fused/separate sweep on the 100-adapter workload: tokens/s of every
     policy at T in {1, 8, 16, 32, 64}; the threshold whose geometric mean over
@@ -319,6 +394,9 @@ def main():
     ap.add_argument("--no-profile", action="store_true", help="skip the per-stage pass")
     ap.add_argument("--route-per-call", action="store_true",
                     help="route every call (lora_apply) instead of once per step (lora_plan_route)")
+    ap.add_argument("--loader", action="store_true",
+                    help="measure adapter load latency through the async loader instead of the bench step")
+    ap.add_argument("--loader-rounds", type=int, default=20)
     ap.add_argument("--theta-sweep", action="store_true",
                     help="run the fused/separate threshold sweep instead of the bench step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -337,6 +415,9 @@ def main():
     from rank_adapter_gemm_token_amd import lora as L
     if args.theta_sweep:
         theta_sweep(L, args)
+        return
+    if args.loader:
+        loader_bench(L, args)
         return
 
     w, steps, desc = setup(args, L)
