@@ -63,6 +63,7 @@ extern "C" {
 typedef struct lora_pool_s *lora_pool; /* opaque; owned by the library */
 typedef struct lora_plan_s *lora_plan; /* opaque routing plan; owned by the library */
 typedef struct lora_loader_s *lora_loader; /* opaque host-to-slot loader; owned by the library */
+typedef struct lora_residency_s *lora_residency; /* opaque slot residency manager */
 
 typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
 
@@ -293,6 +294,54 @@ int lora_load_poll(lora_loader l, uint64_t ticket, int *done);
 /* Blocking: wait for the load's copies, then commit it.  A ticket that was
  * committed already returns LORA_OK.  Errors: LORA_EINVAL, LORA_EHIP. */
 int lora_load_wait(lora_loader l, uint64_t ticket);
+
+/* ----------------------------------------------------------- residency -- */
+
+/* Which adapters stay resident when a pool's slots run out
+ * ["LLM 多 LoRA 推理服务工程 2026", four-layer runtime, storage-pool
+ * paragraph: LRU-K between the HBM tier and the tiers below; "Multi-LoRA 在线
+ * 服务隔离", memory-accounting section: evict only versions with no live
+ * reference, least recently used first, never weights a request holds, per-
+ * tenant resident shares].  The manager takes the slots of pool p that are
+ * FREE now (slots registered outside it are never touched) and loads through
+ * loader l.  k: accesses of history (LRU-K; 2 is the usual choice).
+ * Errors: LORA_EINVAL, LORA_ENOMEM. */
+int lora_residency_create(lora_pool p, lora_loader l, int k, lora_residency *out);
+
+/* Frees the manager; resident adapters stay registered in the pool. */
+int lora_residency_destroy(lora_residency r);
+
+/* Cap on the slots tenant's adapters may hold at once (unset: no cap).
+ * Errors: LORA_EINVAL (tenant < 0, max_slots < 0). */
+int lora_residency_set_share(lora_residency r, int32_t tenant, int max_slots);
+
+/* One more holder of adapter `adapter_id` (the caller's identity of a
+ * version, e.g. a digest) of `tenant`.  Resident: *slot is its slot,
+ * *ticket its load's ticket (0 if committed long ago; lora_load_wait on it
+ * returns at once when done).  Not resident: a slot is chosen (a free one
+ * within the tenant's share, else the LRU-K victim among unreferenced slots,
+ * only the tenant's own when it is at its share), the victim is unloaded
+ * (lora_unregister: drains the applies that may read it) and the adapter is
+ * loaded there with lora_load_async from A_host / B_host (as there); wait on
+ * *ticket before routing tokens to *slot.
+ * Errors: LORA_ESLOT_BUSY (every candidate slot is referenced, or the
+ * tenant's share is 0; nothing changes), LORA_EINVAL (NULL pointers, id
+ * resident for another tenant), and lora_load_async's errors (then the
+ * chosen slot is left empty). */
+int lora_residency_acquire(lora_residency r, uint64_t adapter_id, int32_t tenant, const void *A_host,
+                           const void *B_host, int rank, float alpha, int *slot, uint64_t *ticket);
+
+/* One holder fewer.  Errors: LORA_EINVAL (not resident, or no holder). */
+int lora_residency_release(lora_residency r, uint64_t adapter_id);
+
+/* Counters since creation. */
+typedef struct {
+    uint64_t hits, misses, evictions;
+    int32_t resident;  /* slots holding an adapter of the manager */
+    int32_t managed;   /* slots the manager may use */
+} lora_residency_stats;
+
+int lora_residency_stats_read(lora_residency r, lora_residency_stats *out);
 
 /* ---------------------------------------------------------- observation -- */
 

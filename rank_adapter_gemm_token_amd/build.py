@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "liblora.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "ledger.cpp", "route.hip", "pad_copy.hip", "apply_kernels.hip", "gemm_decode.hip",
+SOURCES = ["api.cpp", "ledger.cpp", "residency.cpp", "route.hip", "pad_copy.hip", "apply_kernels.hip", "gemm_decode.hip",
            "gemm_tiled.hip", "shrink_expand.hip"]
 
 # Packed-fp32 VALU instructions are kept out of every device object.

@@ -20,6 +20,7 @@
 #include "../../include/lora.h"
 #include "internal.hpp"
 #include "ledger.hpp"
+#include "residency.hpp"
 
 namespace {
 
@@ -139,6 +140,16 @@ struct lora_loader_s {
     std::map<uint64_t, Pending> pending;
     uint64_t last_ticket = 0;
     std::mutex mu;
+};
+
+struct lora_residency_s {
+    lora_pool pool = nullptr;
+    lora_loader loader = nullptr;
+    lora::Residency cache;
+    std::vector<uint64_t> ticket;  // [S] the last load's ticket per slot
+    int managed = 0;
+    std::mutex mu;
+    lora_residency_s(int n_slots, int k) : cache(n_slots, k), ticket(static_cast<size_t>(n_slots), 0) {}
 };
 
 namespace {
@@ -830,6 +841,97 @@ int lora_load_wait(lora_loader l, uint64_t ticket) {
     const hipError_t e = hipEventSynchronize(l->done[it->second.buf]);
     if (e != hipSuccess) return hip_fail(e);
     return commit_load(l, ticket);
+}
+
+int lora_residency_create(lora_pool p, lora_loader l, int k, lora_residency *out) {
+    if (out == nullptr) return LORA_EINVAL;
+    *out = nullptr;
+    if (p == nullptr || l == nullptr || k < 1) return LORA_EINVAL;
+    lora_residency r = new (std::nothrow) lora_residency_s(p->S, k);
+    if (r == nullptr) return LORA_ENOMEM;
+    r->pool = p;
+    r->loader = l;
+    std::lock_guard<std::mutex> lk(p->mu);
+    for (int s = 0; s < p->S; ++s) {
+        const bool free_now = p->book.slot(s).state == lora::SlotState::Free;
+        r->cache.set_usable(s, free_now);
+        r->managed += free_now ? 1 : 0;
+    }
+    *out = r;
+    return LORA_OK;
+}
+
+int lora_residency_destroy(lora_residency r) {
+    delete r;
+    return LORA_OK;
+}
+
+int lora_residency_set_share(lora_residency r, int32_t tenant, int max_slots) {
+    if (r == nullptr) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(r->mu);
+    return r->cache.set_share(tenant, max_slots);
+}
+
+int lora_residency_acquire(lora_residency r, uint64_t adapter_id, int32_t tenant, const void *A_host,
+                           const void *B_host, int rank, float alpha, int *slot, uint64_t *ticket) {
+    if (r == nullptr || slot == nullptr || ticket == nullptr) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(r->mu);
+    lora::Residency::Decision d;
+    const int rc = r->cache.acquire(adapter_id, tenant, &d);
+    if (rc != LORA_OK) return rc;
+    if (d.hit) {
+        *slot = d.slot;
+        *ticket = r->ticket[d.slot];
+        return LORA_OK;
+    }
+    if (A_host == nullptr || B_host == nullptr) {
+        r->cache.abandon(d.slot);
+        return LORA_EINVAL;
+    }
+    if (d.evict) {
+        // No holder references the victim.  Its load may still be pending:
+        // finish it, then unload (the unregister drains every apply already
+        // enqueued that might still read it).
+        if (r->ticket[d.slot] != 0) {
+            const int rw = lora_load_wait(r->loader, r->ticket[d.slot]);
+            if (rw != LORA_OK) {
+                r->cache.abandon(d.slot);
+                return rw;
+            }
+        }
+        const int ru = lora_unregister(r->pool, d.slot);
+        if (ru != LORA_OK) {
+            r->cache.abandon(d.slot);
+            return ru;
+        }
+    }
+    uint64_t t = 0;
+    const int rl = lora_load_async(r->loader, r->pool, d.slot, tenant, A_host, B_host, rank, alpha, &t);
+    if (rl != LORA_OK) {
+        r->cache.abandon(d.slot);
+        return rl;
+    }
+    r->ticket[d.slot] = t;
+    *slot = d.slot;
+    *ticket = t;
+    return LORA_OK;
+}
+
+int lora_residency_release(lora_residency r, uint64_t adapter_id) {
+    if (r == nullptr) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(r->mu);
+    return r->cache.release(adapter_id);
+}
+
+int lora_residency_stats_read(lora_residency r, lora_residency_stats *out) {
+    if (r == nullptr || out == nullptr) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(r->mu);
+    out->hits = r->cache.hits;
+    out->misses = r->cache.misses;
+    out->evictions = r->cache.evictions;
+    out->resident = r->cache.occupied();
+    out->managed = r->managed;
+    return LORA_OK;
 }
 
 int lora_pool_stats(lora_pool p, lora_stats *out) {

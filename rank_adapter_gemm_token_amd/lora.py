@@ -44,6 +44,8 @@ EXPORTS = ["lora_pool_create", "lora_pool_destroy", "lora_set_tenant_quota", "lo
            "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_route",
            "lora_plan_create", "lora_plan_destroy", "lora_plan_route", "lora_apply_routed",
            "lora_loader_create", "lora_loader_destroy", "lora_load_async", "lora_load_poll", "lora_load_wait",
+           "lora_residency_create", "lora_residency_destroy", "lora_residency_set_share",
+           "lora_residency_acquire", "lora_residency_release", "lora_residency_stats_read",
            "lora_pool_stats", "lora_tenant_bytes", "lora_poll_errors", "lora_profile_enable",
            "lora_profile_read", "lora_strerror", "lora_last_hip_error"]
 
@@ -59,6 +61,11 @@ class lora_stats(ctypes.Structure):
                 ("last_base_only_tokens", ctypes.c_int32), ("last_invalid_tokens", ctypes.c_int32),
                 ("last_lora_rows_padded", ctypes.c_int64), ("last_lora_rows_true", ctypes.c_int64),
                 ("last_zero_pad_fraction", ctypes.c_double)]
+
+
+class lora_residency_stats(ctypes.Structure):
+    _fields_ = [("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64), ("evictions", ctypes.c_uint64),
+                ("resident", ctypes.c_int32), ("managed", ctypes.c_int32)]
 
 
 class lora_profile(ctypes.Structure):
@@ -88,6 +95,13 @@ _lib.lora_load_async.argtypes = [_vp, _vp, _i, ctypes.c_int32, _vp, _vp, _i, cty
                                  ctypes.POINTER(ctypes.c_uint64)]
 _lib.lora_load_poll.argtypes = [_vp, ctypes.c_uint64, ctypes.POINTER(_i)]
 _lib.lora_load_wait.argtypes = [_vp, ctypes.c_uint64]
+_lib.lora_residency_create.argtypes = [_vp, _vp, _i, ctypes.POINTER(_vp)]
+_lib.lora_residency_destroy.argtypes = [_vp]
+_lib.lora_residency_set_share.argtypes = [_vp, ctypes.c_int32, _i]
+_lib.lora_residency_acquire.argtypes = [_vp, ctypes.c_uint64, ctypes.c_int32, _vp, _vp, _i, ctypes.c_float,
+                                        ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_uint64)]
+_lib.lora_residency_release.argtypes = [_vp, ctypes.c_uint64]
+_lib.lora_residency_stats_read.argtypes = [_vp, ctypes.POINTER(lora_residency_stats)]
 _lib.lora_pool_stats.argtypes = [_vp, ctypes.POINTER(lora_stats)]
 _lib.lora_tenant_bytes.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]
 _lib.lora_poll_errors.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64)]
@@ -303,6 +317,40 @@ def lora_load_poll(loader, ticket):
 
 def lora_load_wait(loader, ticket):
     _check(_lib.lora_load_wait(loader, int(ticket)), "lora_load_wait")
+
+
+def lora_residency_create(pool, loader, k=2):
+    h = _vp()
+    _check(_lib.lora_residency_create(pool, loader, int(k), ctypes.byref(h)), "lora_residency_create")
+    return h.value
+
+
+def lora_residency_destroy(res):
+    _check(_lib.lora_residency_destroy(res), "lora_residency_destroy")
+
+
+def lora_residency_set_share(res, tenant, max_slots):
+    _check(_lib.lora_residency_set_share(res, int(tenant), int(max_slots)), "lora_residency_set_share")
+
+
+def lora_residency_acquire(res, adapter_id, tenant, A_host, B_host, rank, alpha):
+    """Returns (slot, ticket); ticket 0 for an adapter resident and committed."""
+    s, t = _i(), ctypes.c_uint64()
+    _check(_lib.lora_residency_acquire(res, int(adapter_id), int(tenant),
+                                       None if A_host is None else _host_ptr(A_host),
+                                       None if B_host is None else _host_ptr(B_host), int(rank), float(alpha),
+                                       ctypes.byref(s), ctypes.byref(t)), "lora_residency_acquire")
+    return s.value, t.value
+
+
+def lora_residency_release(res, adapter_id):
+    _check(_lib.lora_residency_release(res, int(adapter_id)), "lora_residency_release")
+
+
+def lora_residency_stats_read(res):
+    st = lora_residency_stats()
+    _check(_lib.lora_residency_stats_read(res, ctypes.byref(st)), "lora_residency_stats_read")
+    return {name: getattr(st, name) for name, _ in lora_residency_stats._fields_}
 
 
 def lora_pool_stats(pool):

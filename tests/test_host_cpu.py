@@ -99,6 +99,14 @@ def test_validation_before_device_use():
     d = ctypes.c_int()
     assert lib.lora_load_poll(None, 1, ctypes.byref(d)) == L.LORA_EINVAL
     assert lib.lora_load_wait(None, 1) == L.LORA_EINVAL
+    # Residency: null handles.
+    assert lib.lora_residency_create(None, None, 2, ctypes.byref(h)) == L.LORA_EINVAL
+    assert lib.lora_residency_destroy(None) == L.LORA_OK
+    assert lib.lora_residency_set_share(None, 0, 1) == L.LORA_EINVAL
+    sl = ctypes.c_int()
+    assert lib.lora_residency_acquire(None, 1, 0, None, None, 8, ctypes.c_float(16.0), ctypes.byref(sl),
+                                      ctypes.byref(t)) == L.LORA_EINVAL
+    assert lib.lora_residency_release(None, 1) == L.LORA_EINVAL
 
 
 def test_stats_struct_layout_matches_header(tmp_path):
@@ -123,6 +131,16 @@ def test_slot_book_and_ledger(tmp_path):
     subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-o", str(exe),
                     os.path.join(ROOT, "tests", "native", "ledger_check.cpp"),
                     os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc", "ledger.cpp")],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_residency_policy(tmp_path):
+    exe = tmp_path / "residency_check"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-o", str(exe),
+                    os.path.join(ROOT, "tests", "native", "residency_check.cpp"),
+                    os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc", "residency.cpp")],
                    check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
