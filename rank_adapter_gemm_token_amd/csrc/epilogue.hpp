@@ -185,15 +185,25 @@ struct RowFacts {
     float s[TB];
 };
 
+// row_facts in two stages, so that a caller can put other independent loads
+// between them: the first issues the rows' bucket and token loads, the second
+// (which waits for them) the bucket records and slot entries.
 template <int TB>
-__device__ __forceinline__ void row_facts(const ApplyArgs &a, int p0, int rows_end, RowFacts<TB> &f) {
+__device__ __forceinline__ void row_facts_begin(const ApplyArgs &a, int p0, int rows_end, RowFacts<TB> &f) {
     const int r = threadIdx.x & 15;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const int pc = min(p0 + tb * 16 + r, rows_end - 1);
         f.g[tb] = a.rv.pos_seg[pc];
-        f.tok[tb] = min(max(a.rv.perm[pc], 0), a.T - 1);
+        f.tok[tb] = a.rv.perm[pc];
     }
+}
+
+template <int TB>
+__device__ __forceinline__ void row_facts_end(const ApplyArgs &a, int p0, int rows_end, RowFacts<TB> &f) {
+    const int r = threadIdx.x & 15;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) f.tok[tb] = min(max(f.tok[tb], 0), a.T - 1);
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         f.key[tb] = a.rv.segs[4 * f.g[tb]];
@@ -210,6 +220,26 @@ __device__ __forceinline__ void row_facts(const ApplyArgs &a, int p0, int rows_e
         if (p0 + tb * 16 + r >= rows_end) f.g[tb] = -1;
 }
 
+template <int TB>
+__device__ __forceinline__ void row_facts(const ApplyArgs &a, int p0, int rows_end, RowFacts<TB> &f) {
+    row_facts_begin<TB>(a, p0, rows_end, f);
+    row_facts_end<TB>(a, p0, rows_end, f);
+}
+
+// Raw h of 16 sorted rows p0 .. (clamped to rows_end) for every 32-wide rank
+// step, parts added in order: lane (r, kq) holds row p0 + r, ranks js * 32 +
+// 8 kq .. +7 -- what lora_expand_mfma loads for a one-block tile, fetched
+// early by a caller that has the rows before their routing facts.
+template <int HP = MAX_HPARTS>
+__device__ __forceinline__ void prefetch_h1(const ApplyArgs &a, int p0, int rows_end, float (&hv)[2][8]) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;
+    const int kq = lane >> 4;
+    const int row = min(p0 + r, rows_end - 1);
+#pragma unroll
+    for (int js = 0; js < 2; ++js) load_h8<HP>(a, row, min(js * 32 + 8 * kq, a.R - 8), hv[js]);
+}
+
 // Adds s_g * h[p][:] . B_g[n][:] to acc for every row p of the wave tile whose
 // bucket g has mode `want` (FUSED inside the base GEMM, SEPARATE in the
 // residual kernel).  The wave tile is TB blocks of 16 sorted rows starting at
@@ -223,7 +253,8 @@ __device__ __forceinline__ void row_facts(const ApplyArgs &a, int p0, int rows_e
 // is a run of lanes), one round of B loads per bucket.
 template <int DT, int TB, int WC, int HP = MAX_HPARTS>
 __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int rows_end, int n0, int want,
-                                                 const RowFacts<TB> &f, f32x4_t (&acc)[TB][WC]) {
+                                                 const RowFacts<TB> &f, f32x4_t (&acc)[TB][WC],
+                                                 const float (*hpre)[8] = nullptr) {
     using E = Elem<DT>;
     using V = typename E::vec8;
     using raw = typename E::raw;
@@ -243,7 +274,13 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
 
     // Raw h of block tb's rows for rank step js (unconditional loads:
     // clamped row and rank).
+    // (hpre: the one block's h, prefetched by the caller with prefetch_h1.)
     auto load_h = [&](int tb, int js, float (&hv)[8]) {
+        if (TB == 1 && hpre != nullptr) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hv[e] = hpre[js][e];
+            return;
+        }
         const int hrow = a.h_by_token ? f.tok[tb] : min(p0 + tb * 16 + r, rows_end - 1);
         load_h8<HP>(a, hrow, min(js * 32 + 8 * kq, Rp - 8), hv);
     };

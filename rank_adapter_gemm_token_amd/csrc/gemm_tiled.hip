@@ -361,14 +361,20 @@ __global__ __launch_bounds__(256) void k_split_epilogue(ApplyArgs a, const float
     const int cb0 = static_cast<int>(blockIdx.x) * 4;
     const f32x4_t *p = reinterpret_cast<const f32x4_t *>(part) + (static_cast<size_t>(rb) * ncb + cb0) * 64 + lane;
     const size_t zs = static_cast<size_t>(nrb) * ncb * 64;
-    // Every split's loads issued at once (split index clamped; repeats are
-    // not added), so the wait counts stay exact.
+    // Everything that does not depend on the routing facts is requested
+    // before them, behind their first round: the rows' buckets and tokens,
+    // then every split's partials (split index clamped, repeats not added, so
+    // the wait counts stay exact) and the rows' h.
+    RowFacts<1> f;
+    row_facts_begin<1>(a, rb * 16, a.T, f);
     f32x4_t v[MAX_TSPLIT][4];
 #pragma unroll
     for (int z = 0; z < MAX_TSPLIT; ++z)
 #pragma unroll
         for (int wc = 0; wc < 4; ++wc) v[z][wc] = p[min(z, splits - 1) * zs + wc * 64];
-    asm volatile("" ::: "memory");
+    float hpre[2][8];
+    prefetch_h1(a, rb * 16, a.T, hpre);
+    row_facts_end<1>(a, rb * 16, a.T, f);
     f32x4_t acc[1][4];
 #pragma unroll
     for (int wc = 0; wc < 4; ++wc) {
@@ -377,9 +383,7 @@ __global__ __launch_bounds__(256) void k_split_epilogue(ApplyArgs a, const float
         for (int z = 1; z < MAX_TSPLIT; ++z)
             if (z < splits) acc[0][wc] += v[z][wc];
     }
-    RowFacts<1> f;
-    row_facts<1>(a, rb * 16, a.T, f);
-    lora_expand_mfma<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, SEG_FUSED, f, acc);
+    lora_expand_mfma<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, SEG_FUSED, f, acc, hpre);
     store_rows<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, f, acc);
 }
 

@@ -105,3 +105,43 @@ def test_small_ragged_full(dtype, T, d_in, d_out, S, R, policy):
         assert p.poll_errors() == int(inv.sum())
     finally:
         p.close()
+
+
+def _max_case(dtype, T, d_in, d_out, S, R, used, seed):
+    """S slots of which only `used` (spread over the whole range, up to slot
+    S - 1) hold adapters; tokens name those, base_only and invalid slots."""
+    rng = np.random.default_rng(seed)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    x = torch.from_numpy(rng.standard_normal((T, d_in))).to(tdt)
+    W = torch.from_numpy(rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).to(tdt)
+    slots = sorted(set([S - 1, 0] + rng.choice(S, size=used - 2, replace=False).tolist()))
+    ads = []
+    for s in slots:
+        r = int(rng.integers(1, R + 1))
+        ads.append(wl.Adapter(s, s % 3, r, float(2 * r),
+                              torch.from_numpy(rng.standard_normal((r, d_in)) / np.sqrt(d_in)).to(tdt),
+                              torch.from_numpy(rng.standard_normal((d_out, r)) * 0.1).to(tdt)))
+    choice = np.array(slots + [-1, S + 5, 1 if 1 not in slots else S])  # incl. base_only and invalid
+    idx = torch.from_numpy(choice[rng.integers(0, len(choice), size=T)].astype(np.int32))
+    return x, W, ads, idx
+
+
+# The largest pool (LORA_MAX_SLOTS slots, LORA_MAX_RANK rank) on every path:
+# decode (d_out = 128: two column groups take slots 0..1023 in turn), the split
+# 256-row tiles and the unsplit ones (a call of 4100 tokens, rows sampled).
+@pytest.mark.parametrize("dtype,T,d_in,d_out", [("f16", 64, 256, 128), ("bf16", 700, 256, 256),
+                                                ("bf16", 4100, 256, 256), ("f32", 33, 64, 64)])
+def test_max_slots_and_rank(dtype, T, d_in, d_out):
+    S, R = lora.LORA_MAX_SLOTS, lora.LORA_MAX_RANK
+    x, W, ads, idx = _max_case(dtype, T, d_in, d_out, S, R, used=40, seed=T)
+    p = Pool(d_in, d_out, R, S, T, dtype)
+    try:
+        p.register_all(ads)
+        y = p.apply(dev(x), dev(W), dev(idx))
+        torch.cuda.synchronize()
+        rows = None if T <= 1024 else sample_rows(T, 64, seed=1, must=[0, T - 1])
+        y_ref, inv = reference(p, x, W, idx, rows=rows)
+        got = y.cpu() if rows is None else y.cpu()[torch.as_tensor(rows)]
+        assert_close(got, y_ref, inv, dtype)
+    finally:
+        p.close()
