@@ -419,7 +419,8 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int w = 1; w < NWK; ++w) v += red[(w * NB + f) * 64 + lane];
         const int tb = f / DCB, c = f % DCB;
-        part[((static_cast<size_t>(q) * (a.d_out / 16) + c0 / 16 + c) * TB + tb) * 64 + lane] = v;
+        // Streaming store: the epilogue reads the partials once, on other XCDs.
+        __builtin_nontemporal_store(v, &part[((static_cast<size_t>(q) * (a.d_out / 16) + c0 / 16 + c) * TB + tb) * 64 + lane]);
     }
 
     // 5. Shrink results: this split's part of h = x . A_s^T for the rows of

@@ -332,7 +332,8 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
         store_rows<DT, TB, WC>(a, pw, a.T, nw, f, acc);
     } else {
         // Partial sums [z][16-row block][16-column block][lane], row blocks
-        // of sorted rows below T only.
+        // of sorted rows below T only; streaming stores (read once, by the
+        // split epilogue).
         const int nrb = (a.T + 15) / 16, ncb = a.d_out / 16;
         f32x4_t *pz = reinterpret_cast<f32x4_t *>(part) + static_cast<size_t>(blockIdx.z) * nrb * ncb * 64;
 #pragma unroll
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
             if (rb < nrb) {
 #pragma unroll
                 for (int wc = 0; wc < WC; ++wc)
-                    pz[(static_cast<size_t>(rb) * ncb + nw / 16 + wc) * 64 + lane] = acc[tb][wc];
+                    __builtin_nontemporal_store(acc[tb][wc], &pz[(static_cast<size_t>(rb) * ncb + nw / 16 + wc) * 64 + lane]);
             }
         }
     }
