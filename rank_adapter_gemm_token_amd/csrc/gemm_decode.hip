@@ -219,6 +219,11 @@ __device__ __forceinline__ void publish_route(const SmallRoute &sr, int T, const
 
 using lds_ptr = __attribute__((address_space(3))) void *;
 
+// Cache policy of the W loads: non-temporal.  W is read once per call;
+// streamed through L2 with the default policy it evicts the x tile that
+// every column group of a split reads.
+constexpr int CPOL_NT = 2;
+
 // Waits until at most N vector-memory operations of this wave are
 // outstanding (they complete in order), and keeps the compiler from moving
 // memory accesses across the wait.
@@ -253,7 +258,7 @@ __device__ __forceinline__ void issue_pair(const __amdgpu_buffer_rsrc_t &xrs, co
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(slot + g * 64), 16, loff[g], soff, 0, 0);
 #pragma unroll
     for (int g = nx; g < nl; ++g)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(slot + g * 64), 16, loff[g], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(slot + g * 64), 16, loff[g], soff, 0, CPOL_NT);
     __builtin_amdgcn_sched_barrier(0);
 }
 
