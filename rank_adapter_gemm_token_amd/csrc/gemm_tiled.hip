@@ -150,6 +150,29 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
 // k_split_epilogue adds them.
 using lds_ptr = __attribute__((address_space(3))) void *;
 
+// Byte offset of an LDS object.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
+}
+
+// 16-byte LDS read at byte offset `addr`, issued as inline assembly: its
+// result is usable only after an lgkmcnt wait (lgkm_wait) and pin().
+__device__ __forceinline__ u32x4_t ds_read16(uint32_t addr) {
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// Waits until at most N LDS reads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+
+// Orders every use of v after the preceding lgkm_wait (both are volatile
+// statements, which keep their order).
+__device__ __forceinline__ void pin(u32x4_t &v) { asm volatile("" : "+v"(v)); }
+
 // Output tile of workgroup `id` (of nx x ny): workgroups are dealt to the 8
 // XCDs round-robin (id mod 8), so XCD k takes the k-th eighth of a grouped
 // order -- 4 row tiles at a time, column by column -- and its workgroups share
@@ -252,21 +275,44 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // The operand reads are inline ds_read_b128, ordered after their own
+    // lgkmcnt wait: the compiler then sees no LDS read that could alias the
+    // buffer loads into LDS still in flight, and adds no wait for them of its
+    // own (it would wait for every outstanding load -- the next stages' too).
     auto compute = [&](const u32x4_t *buf) {
+        const uint32_t base = lds_offset(buf);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int lo = ks ? lo1 : lo0;
-            V bf[WC];
+            const uint32_t xa = base + static_cast<uint32_t>((wm * TB) * RBU + lo) * 16;
+            const uint32_t wa = base + static_cast<uint32_t>(BOFF + (wn * WC) * RBU + lo) * 16;
+            // W fragments of the step, then x fragments two row blocks at a
+            // time: the next pair's reads are issued before this pair's MFMAs.
+            u32x4_t bq[WC], aq[TB];
 #pragma unroll
-            for (int wc = 0; wc < WC; ++wc) bf[wc] = __builtin_bit_cast(V, buf[BOFF + (wn * WC + wc) * RBU + lo]);
+            for (int wc = 0; wc < WC; ++wc) bq[wc] = ds_read16(wa + wc * RBU * 16);
+            aq[0] = ds_read16(xa);
+            aq[1] = ds_read16(xa + RBU * 16);
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const V af = __builtin_bit_cast(V, buf[(wm * TB + tb) * RBU + lo]);
+            for (int tp = 0; tp < TB; tp += 2) {
+                lgkm_wait<0>();
+                if (tp == 0) {
 #pragma unroll
-                for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(af, bf[wc], acc[tb][wc]);
-                // One row block at a time: keeps the operands of only a few
-                // blocks live next to the accumulators.
-                if (tb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+                    for (int wc = 0; wc < WC; ++wc) pin(bq[wc]);
+                }
+                pin(aq[tp]);
+                pin(aq[tp + 1]);
+                if (tp + 2 < TB) {
+                    aq[tp + 2] = ds_read16(xa + (tp + 2) * RBU * 16);
+                    aq[tp + 3] = ds_read16(xa + (tp + 3) * RBU * 16);
+                }
+#pragma unroll
+                for (int tb = tp; tb < tp + 2; ++tb)
+#pragma unroll
+                    for (int wc = 0; wc < WC; ++wc)
+                        acc[tb][wc] = E::mfma(__builtin_bit_cast(V, aq[tb]), __builtin_bit_cast(V, bq[wc]), acc[tb][wc]);
+                // The pair's MFMAs are issued before the next wait.
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
@@ -284,7 +330,11 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
             if (BLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
             else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         }
-        __syncthreads();
+        // A bare barrier: __syncthreads() adds a workgroup fence, for which
+        // the compiler waits on every outstanding load, the next stage's too.
+        // This wave's reads of the buffer the next issue overwrites returned
+        // before its last MFMAs were issued.
+        __builtin_amdgcn_s_barrier();
     };
 
     const int nst = s_end - s_beg;
