@@ -249,25 +249,71 @@ def traffic_for(workload_key, kind):
 # CPU baseline: the oracle on host cores, bounded sample of the same workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(w, seconds):
-    import oracle
-    lin = w.linears[0]
-    cores = len(os.sched_getaffinity(0))
-    x = oracle.to_f64(w.x[lin.d_in])
-    W = oracle.to_f64(lin.W)
-    idx = w.idx.numpy()
-    ads = {a.slot: (oracle.to_f64(a.A), oracle.to_f64(a.B), a.rank, a.alpha) for a in lin.adapters}
-    oracle.apply(x[:1], W, idx[:1], w.S, ads, n_threads=cores)  # load + first touch
+def _oracle_rate(oracle, x, W, idx, S, ads, cores, seconds):
+    """Full oracle calls of one linear on the given token rows for about
+    `seconds`: (calls, elapsed s)."""
+    oracle.apply(x[:1], W, idx[:1], S, ads, n_threads=cores)  # load + first touch
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.apply(x, W, idx, w.S, ads, n_threads=cores)
+        oracle.apply(x, W, idx, S, ads, n_threads=cores)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    return {"value": w.T * reps / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d full calls of the %s linear (%d tokens each, fp64, %.1f s)"
-                      % (reps, lin.name, w.T, el)}
+            return reps, el
+
+
+def cpu_baseline(w, seconds, workload):
+    """The fp64 oracle on this host's cores over a bounded sample of the same
+    workload, as tokens/s of one bench step (all the step's linears)."""
+    import oracle
+    from rank_adapter_gemm_token_amd import workloads as wl
+    cores = len(os.sched_getaffinity(0))
+    idx_all = w.idx.numpy()
+
+    def prep(lin, rows):
+        xt = w.x[lin.d_in]
+        x = oracle.to_f64(xt[torch.as_tensor(rows, device=xt.device)])
+        ads = {a.slot: (oracle.to_f64(a.A), oracle.to_f64(a.B), a.rank, a.alpha) for a in lin.adapters}
+        return x, oracle.to_f64(lin.W), idx_all[rows], ads
+
+    if workload == "prefill":
+        # Every 16th token (256 of 4096, all eight sequences and their
+        # adapters) through both projections; a step is the q+v pair.
+        rows = np.arange(0, w.T, 16)
+        per_lin = []
+        for lin in w.linears:
+            x, W, idx, ads = prep(lin, rows)
+            reps, el = _oracle_rate(oracle, x, W, idx, w.S, ads, cores, seconds / len(w.linears))
+            per_lin.append(el / (reps * len(rows)))
+        value = 1.0 / sum(per_lin)
+        sample = ("%d of the %d tokens (every 16th) through q_proj and v_proj, fp64, %.1f s"
+                  % (len(rows), w.T, seconds))
+    elif workload == "stack":
+        # 8 tokens through one linear of each shape (layer 0's q_proj, gate_proj,
+        # down_proj); a step is 32 layers x (4 q-shaped + 2 gate-shaped + 1
+        # down-shaped) linears, all of the same cost per token as the sample's.
+        # The bench setup hands the weights to the pools, so the three linears
+        # are drawn again from their seeds.
+        rows = np.arange(0, w.T, w.T // 8)
+        per_tok = 0.0
+        for proj, count in ((0, 4), (4, 2), (6, 1)):  # q_proj, gate_proj, down_proj
+            lin = wl.stack_linear(0, proj, w.x[4096].device, w.seed, w.S, w.R)
+            x, W, idx, ads = prep(lin, rows)
+            del lin
+            reps, el = _oracle_rate(oracle, x, W, idx, w.S, ads, cores, seconds / 3)
+            per_tok += count * el / (reps * len(rows))
+        n_layers = len(w.linears) // 7
+        value = 1.0 / (n_layers * per_tok)
+        sample = ("%d tokens through one q_proj, gate_proj and down_proj (fp64, %.1f s), scaled to the "
+                  "%d-linear step" % (len(rows), seconds, len(w.linears)))
+    else:
+        lin = w.linears[0]
+        rows = np.arange(w.T)
+        x, W, idx, ads = prep(lin, rows)
+        reps, el = _oracle_rate(oracle, x, W, idx, w.S, ads, cores, seconds)
+        value = w.T * reps / el
+        sample = "%d full calls of the %s linear (%d tokens each, fp64, %.1f s)" % (reps, lin.name, w.T, el)
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "sample": sample}
 
 
 # ----------------------------------------------------------------------------
@@ -481,8 +527,8 @@ def main():
         roof["traffic"] = traffic_for(args.workload, kind)
 
     cpu = None
-    if not args.no_cpu_baseline and (args.workload == "decode" or args.workload.startswith("sweep")):
-        cpu = cpu_baseline(w, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds, args.workload)
         log("cpu baseline:", cpu)
 
     # The rank-padding share of the batch's LoRA rows (the shrink and expand
