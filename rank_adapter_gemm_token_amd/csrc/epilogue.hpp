@@ -390,4 +390,30 @@ __device__ __forceinline__ void store_rows(const ApplyArgs &a, int p0, int rows_
     }
 }
 
+// store_rows with each row's token read from `rowtok` (row p0 + i at
+// rowtok[i], in LDS; the bitwise NOT of the token marks a row of the invalid
+// bucket, stored as NaN).
+template <int DT, int TB, int WC>
+__device__ __forceinline__ void store_rows_tok(const ApplyArgs &a, int p0, int rows_end, int n0, const int *rowtok,
+                                               const f32x4_t (&acc)[TB][WC]) {
+    using E = Elem<DT>;
+    using raw = typename E::raw;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;
+    const int kq = lane >> 4;
+    raw *y = static_cast<raw *>(a.y);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = p0 + tb * 16 + kq * 4 + i;
+            if (p >= rows_end) continue;
+            const int v = rowtok[tb * 16 + kq * 4 + i];
+            const size_t base = static_cast<size_t>(v < 0 ? ~v : v) * a.d_out + n0 + r;
+#pragma unroll
+            for (int wc = 0; wc < WC; ++wc) y[base + wc * 16] = v < 0 ? E::qnan : E::from_f(acc[tb][wc][i]);
+        }
+    }
+}
+
 }  // namespace lora

@@ -206,6 +206,9 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     __shared__ u32x4_t lds0[(16 + NBW) * RBU];
     __shared__ u32x4_t lds1[(16 + NBW) * RBU];
     __shared__ u32x4_t lds2[NBUF == 3 ? (16 + NBW) * RBU : 1];
+    // Output token of each sorted row of the tile (bitwise NOT of it for rows
+    // of the invalid bucket), for the epilogue's stores.
+    __shared__ int rowtok[SPLIT ? 1 : BM];
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -337,9 +340,28 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
         __builtin_amdgcn_s_barrier();
     };
 
+    // SPLIT = false: the LoRA term s * h * B of the tile's FUSED rows is the
+    // accumulators' starting value, computed while the first stage loads (the
+    // main loop then adds x W^T to it; one rounding at the end either way).
+    // Done here, the expand's registers are not live across the main loop.
+    auto lora_prologue = [&]() {
+        const int pw0 = m0 + wm * TB * 16;
+        RowFacts<TB> f;
+        row_facts<TB>(a, pw0, a.T, f);
+        // Calls this large take one shrink part (tiled_h_parts).
+        lora_expand_mfma<DT, TB, WC, 1>(a, pw0, a.T, n0 + wn * WC * 16, SEG_FUSED, f, acc);
+        if (wn == 0 && g == 0) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+                rowtok[wm * TB * 16 + tb * 16 + r] = f.key[tb] == a.S + 1 ? ~f.tok[tb] : f.tok[tb];
+        }
+        __syncthreads();
+    };
+
     const int nst = s_end - s_beg;
     if (NBUF == 2) {
         issue(s_beg, lds0);
+        if constexpr (!SPLIT) lora_prologue();
         for (int j = 0; j < nst; j += 2) {
             sync_stage(false);
             if (j + 1 < nst) issue(s_beg + j + 1, lds1);
@@ -374,12 +396,9 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     int pw = m0 + wm * TB * 16;
     asm volatile("" : "+s"(pw));
     const int nw = n0 + wn * WC * 16;
-    if (!SPLIT) {
-        RowFacts<TB> f;
-        row_facts<TB>(a, pw, a.T, f);
-        // Calls this large take one shrink part (tiled_h_parts).
-        lora_expand_mfma<DT, TB, WC, 1>(a, pw, a.T, nw, SEG_FUSED, f, acc);
-        store_rows<DT, TB, WC>(a, pw, a.T, nw, f, acc);
+    if constexpr (!SPLIT) {
+        static_assert(NBUF == 2, "the LoRA prologue runs in the two-buffer loop");
+        store_rows_tok<DT, TB, WC>(a, pw, a.T, nw, rowtok + wm * TB * 16, acc);
     } else {
         // Partial sums [z][16-row block][16-column block][lane], row blocks
         // of sorted rows below T only; streaming stores (read once, by the
