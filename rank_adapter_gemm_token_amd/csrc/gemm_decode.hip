@@ -330,8 +330,9 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     //    8 rows, 8 lanes a row covering its 128-byte line; the chunk a lane
     //    fetches is XOR-swizzled by the row within its 16-row block, so the
     //    chunk at position m of row rho is chunk m ^ sw(rho), sw(rho) =
-    //    (rho & 7) ^ (rho >> 3).  x rows past T repeat row T - 1 (their
-    //    outputs are never used).
+    //    rho & 7, which keeps the operand reads free of bank conflicts (the
+    //    same layout as the LDS-staged tiled GEMM).  x rows past T repeat row
+    //    T - 1 (their outputs are never used).
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(T) * rowb);
     const __amdgpu_buffer_rsrc_t wrs =
         make_rsrc(static_cast<const uint16_t *>(a.W) + static_cast<size_t>(c0) * a.d_in, DCOLS * rowb);
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int g = 0; g < L; ++g) {
         const int rho = 8 * (g & 1) + (lane >> 3);   // row within its 16-row block
-        const int chunk = (lane & 7) ^ (rho & 7) ^ (rho >> 3);
+        const int chunk = (lane & 7) ^ (rho & 7);
         const int row = 8 * g + (lane >> 3);         // row of the slot: x rows first, then W
         const int src = row < Ring::XROWS ? min(row, T - 1) : row - Ring::XROWS;
         loff[g] = static_cast<uint32_t>(src) * rowb + chunk * 16;
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     // 3. Base GEMM (and the shrink of slot cg) pair by pair.  Operand reads:
     //    lane (r, kq) of half h takes row r of a block, chunk 4 h + kq, at
     //    position (4 h + kq) ^ sw(r).
-    const int sw = (r & 7) ^ (r >> 3);
+    const int sw = r & 7;
     const int lo[2] = {r * 8 + ((0 + kq) ^ sw), r * 8 + ((4 + kq) ^ sw)};
     f32x4_t acc[TB][DCB];
     f32x4_t hacc[TB][RB];
