@@ -329,6 +329,50 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
         }
         return;
     }
+    // One row block (the split-sum and residual kernels): the block's buckets
+    // NBB at a time, the B fragments of a batch requested together, so that a
+    // block of many short buckets waits for ceil(buckets / NBB) rounds of B
+    // loads instead of one per bucket.
+    if constexpr (TB == 1) {
+        constexpr int NBB = 4;
+        float hv[JM][8];
+#pragma unroll
+        for (int js = 0; js < JM; ++js) load_h(0, js, hv[js]);
+        const int last = min(15, rows_end - 1 - p0);
+        const int g0 = uniform(f.g[0]);
+        const int g1 = __builtin_amdgcn_readlane(f.g[0], last);
+        for (int gb = g0; gb <= g1; gb += NBB) {
+            int keys[NBB], rks[NBB];
+            bool use[NBB];
+#pragma unroll
+            for (int b = 0; b < NBB; ++b) {
+                const unsigned long long m = __ballot(f.g[0] == gb + b) & 0xFFFFull;
+                const int l0 = m ? __ffsll(static_cast<long long>(m)) - 1 : 0;
+                const int key = __builtin_amdgcn_readlane(f.key[0], l0);
+                const int mode = __builtin_amdgcn_readlane(f.mode[0], l0);
+                rks[b] = __builtin_amdgcn_readlane(f.rank[0], l0);
+                use[b] = gb + b <= g1 && m != 0 && key < a.S && mode == want;
+                keys[b] = key;
+            }
+#pragma unroll
+            for (int js = 0; js < JM; ++js) {
+                if (js * 32 >= Rp) break;
+                V bf[NBB][WC];
+#pragma unroll
+                for (int b = 0; b < NBB; ++b)
+                    if (use[b] && js * 32 < rks[b]) load_b(keys[b], js, bf[b]);
+#pragma unroll
+                for (int b = 0; b < NBB; ++b) {
+                    if (use[b] && js * 32 < rks[b]) {
+                        const V h = make_h(0, js, gb + b, hv[js]);
+#pragma unroll
+                        for (int wc = 0; wc < WC; ++wc) acc[0][wc] = E::mfma(h, bf[b][wc], acc[0][wc]);
+                    }
+                }
+            }
+        }
+        return;
+    }
     // Otherwise block by block, bucket by bucket.
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
