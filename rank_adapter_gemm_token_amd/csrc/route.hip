@@ -45,6 +45,7 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     __shared__ int s_tot[4];  // buckets, tiles, fused buckets, separate buckets
     __shared__ int s_rows[2]; // padded rows, true rows
     __shared__ unsigned char s_act[MAX_KEYS];     // slot k is ACTIVE
+    __shared__ unsigned short s_rank[MAX_KEYS];   // slot k's true rank
     __shared__ unsigned short s_key[KEY_CAP];     // token -> key (T <= KEY_CAP)
 
     const int K = S + 2;
@@ -52,6 +53,19 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
+    // The first round of token indices and every slot's state and rank are
+    // requested together, before the LDS set-up, in one round trip.  (T = 0:
+    // no index is read.)
+    int vi[IDX_UNROLL] = {};
+    if (T > 0) {
+#pragma unroll
+        for (int u = 0; u < IDX_UNROLL; ++u) vi[u] = idx[min(u * RT + tid, T - 1)];
+    }
+    for (int k = tid; k < S; k += RT) {
+        const SlotDev sd = slots[k];
+        s_act[k] = sd.state == SLOT_ACTIVE;
+        s_rank[k] = static_cast<unsigned short>(sd.rank);
+    }
     for (int k = tid; k < K; k += RT) {
         s_cnt[k] = 0;
         s_run[k] = 0;
@@ -61,21 +75,20 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     if (tid < 2) s_rows[tid] = 0;
     __syncthreads();
 
-    // Keys.  Every slot's state goes to LDS and every index is read once
-    // (IDX_UNROLL per thread in flight); a token's key is then an LDS
-    // lookup, kept in LDS for the scatter when T <= KEY_CAP.
+    // Keys.  Every index is read once (IDX_UNROLL per thread in flight); a
+    // token's key is an LDS lookup of its slot's state, kept in LDS for the
+    // scatter when T <= KEY_CAP.
     const bool keep = T <= KEY_CAP;
-    for (int k = tid; k < S; k += RT) s_act[k] = slots[k].state == SLOT_ACTIVE;
-    __syncthreads();
     for (int t0 = 0; t0 < T; t0 += RT * IDX_UNROLL) {
-        int v[IDX_UNROLL];
+        if (t0 > 0) {
 #pragma unroll
-        for (int u = 0; u < IDX_UNROLL; ++u) v[u] = idx[min(t0 + u * RT + tid, T - 1)];
+            for (int u = 0; u < IDX_UNROLL; ++u) vi[u] = idx[min(t0 + u * RT + tid, T - 1)];
+        }
 #pragma unroll
         for (int u = 0; u < IDX_UNROLL; ++u) {
             const int t = t0 + u * RT + tid;
             if (t >= T) continue;
-            const int key = (v[u] == -1) ? S : ((v[u] >= 0 && v[u] < S && s_act[v[u]]) ? v[u] : S + 1);
+            const int key = (vi[u] == -1) ? S : ((vi[u] >= 0 && vi[u] < S && s_act[vi[u]]) ? vi[u] : S + 1);
             if (keep) s_key[t] = static_cast<unsigned short>(key);
             atomicAdd(&s_cnt[key], 1);  // integer LDS atomics: counts do not depend on order
         }
@@ -135,11 +148,11 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
                 mode = (policy == 1) ? 1 : (policy == 2) ? 2 : (n > theta ? 1 : 2);
                 atomicAdd(&s_tot[mode == 1 ? 2 : 3], 1);
                 atomicAdd(&s_rows[0], n * R);
-                atomicAdd(&s_rows[1], n * slots[k].rank);
+                atomicAdd(&s_rows[1], n * s_rank[k]);
                 if (out.tiles != nullptr) {
                     const int nt = (n + TILE_ROWS - 1) / TILE_ROWS;
                     for (int j = 0; j < nt; ++j) {
-                        out.tiles[2 * (s_tile[k] + j)] = tile_pack(s_seg[k], slots[k].rank);
+                        out.tiles[2 * (s_tile[k] + j)] = tile_pack(s_seg[k], s_rank[k]);
                         out.tiles[2 * (s_tile[k] + j) + 1] = s_off[k] + j * TILE_ROWS;
                     }
                 }
