@@ -84,7 +84,9 @@ def _small_case(dtype, T, d_in, d_out, S, R, seed):
 # register-staged tiles (ragged d_in / d_out), the split-K 256-row tiles
 # (T 65 .. 2047 with d_in, d_out multiples of 128; 4 and 2 splits here) and
 # the unsplit 256 x 256 tiles (T >= 2048), each with a ragged last tile; the
-# last two hold many adapter buckets in every 256-row tile.
+# 2200- and 2300-token cases hold many adapter buckets in every 256-row tile;
+# the last two have enough 16-row bucket tiles (>= 256) for the shrink to take
+# four tiles a workgroup, with bucket boundaries inside some of the groups.
 # Decode calls also cover pools beyond the epilogue's small-pool B tile (S R
 # > 1024) and beyond 64 slots (routing loads each token's slot entry; the GEMM
 # takes slots past its column groups in a second pass).
@@ -93,7 +95,8 @@ def _small_case(dtype, T, d_in, d_out, S, R, seed):
                                                (77, 192, 128, 9, 16), (300, 256, 320, 17, 64),
                                                (513, 64, 128, 40, 24), (200, 1024, 384, 7, 16),
                                                (1000, 512, 512, 11, 32), (2100, 256, 256, 3, 8),
-                                               (2200, 256, 256, 40, 16), (2300, 512, 256, 60, 64)])
+                                               (2200, 256, 256, 40, 16), (2300, 512, 256, 60, 64),
+                                               (4100, 256, 256, 7, 64), (4096, 128, 128, 30, 24)])
 @pytest.mark.parametrize("policy", [0, 1, 2])
 def test_small_ragged_full(dtype, T, d_in, d_out, S, R, policy):
     x, W, ads, idx = _small_case(dtype, T, d_in, d_out, S, R, seed=T * 31 + S)
