@@ -1,5 +1,11 @@
-// gemm_tiled.hip -- base projection for prefill-shaped calls (T > 64 tokens,
-// fp16/bf16) with the fused LoRA expand in its epilogue.
+// gemm_tiled.hip -- base projection for calls of more than 64 tokens
+// (fp16/bf16) with the fused LoRA term.  Three kernels:
+//   * k_gemm_lds<256> (>= 2048 tokens): 256 x 256 tiles staged into LDS by
+//     direct loads, the LoRA term computed into the accumulators before the
+//     main loop (described at its definition);
+//   * k_gemm_lds<128, split> + k_split_epilogue (65 .. 2047 tokens): the same
+//     staging over k ranges, fp32 partial sums, then sum + fused expand;
+//   * k_gemm_tiled (shapes off the 128 grid), described here.
 //
 // Here the projection is a dense contraction with enough rows to be bound by
 // the matrix cores, not by HBM, so both operands are reused from LDS:
