@@ -244,7 +244,13 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     // offset as the scalar offset, one 32-bit lane offset per instruction;
     // the row permutation is read once, in one batch.
     const bool xw = wave < 4;
-    const int nld = xw ? 8 : BLD;
+    // Split calls (T < 2048, so a tile is often mostly past T): an x wave
+    // whose 64 rows all lie past T loads nothing (its stage waits then have
+    // nothing to wait for), and the waves computing those rows skip their
+    // MFMAs (rows past T are never stored).  Not in the unsplit kernel: the
+    // branch around its MFMAs makes the compiler spill the accumulators.
+    const int nld = xw ? ((SPLIT && m0 + (wave & 3) * 64 >= a.T) ? 0 : 8) : BLD;
+    const bool rows_live = !SPLIT || m0 + wm * TB * 16 < a.T;
     const __amdgpu_buffer_rsrc_t rs =
         xw ? make_rsrc(a.x, static_cast<uint32_t>(a.T) * a.d_in * 2)
            : make_rsrc(a.W, static_cast<uint32_t>(a.d_out) * a.d_in * 2);
@@ -377,11 +383,11 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
         for (int j = 0; j < nst; j += 2) {
             sync_stage(false);
             if (j + 1 < nst) issue(s_beg + j + 1, lds1);
-            compute(lds0);
+            if (rows_live) compute(lds0);
             if (j + 1 < nst) {
                 sync_stage(false);
                 if (j + 2 < nst) issue(s_beg + j + 2, lds0);
-                compute(lds1);
+                if (rows_live) compute(lds1);
             }
         }
     } else {
@@ -390,15 +396,15 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
         for (int j = 0; j < nst; j += 3) {
             sync_stage(j + 1 < nst);
             if (j + 2 < nst) issue(s_beg + j + 2, lds2);
-            compute(lds0);
+            if (rows_live) compute(lds0);
             if (j + 1 >= nst) break;
             sync_stage(j + 2 < nst);
             if (j + 3 < nst) issue(s_beg + j + 3, lds0);
-            compute(lds1);
+            if (rows_live) compute(lds1);
             if (j + 2 >= nst) break;
             sync_stage(j + 3 < nst);
             if (j + 4 < nst) issue(s_beg + j + 4, lds1);
-            compute(lds2);
+            if (rows_live) compute(lds2);
         }
     }
 
