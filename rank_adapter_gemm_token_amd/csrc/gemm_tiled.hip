@@ -436,17 +436,19 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
 }
 
 // Split sums of k_gemm_lds<.., true>: workgroup of 4 waves over 64 sorted rows
-// x 64 columns, wave w = rows (4 blockIdx.y + w) * 16 .. +15.  Adds the
+// x 16 WC columns, wave w = rows (4 blockIdx.y + w) * 16 .. +15.  Adds the
 // splits' partial sums in a fixed order, then the fused expand and the
-// scatter to token order, as the unsplit kernel's epilogue does.
-template <int DT>
+// scatter to token order, as the unsplit kernel's epilogue does.  WC = 2 for
+// calls of at most 256 tokens (twice the waves in flight for the same work),
+// else 4.
+template <int DT, int WC>
 __global__ __launch_bounds__(256) void k_split_epilogue(ApplyArgs a, const float *part, int splits) {
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int rb = static_cast<int>(blockIdx.y) * 4 + wave;
     const int nrb = (a.T + 15) / 16, ncb = a.d_out / 16;
     if (rb >= nrb) return;
-    const int cb0 = static_cast<int>(blockIdx.x) * 4;
+    const int cb0 = static_cast<int>(blockIdx.x) * WC;
     const f32x4_t *p = reinterpret_cast<const f32x4_t *>(part) + (static_cast<size_t>(rb) * ncb + cb0) * 64 + lane;
     const size_t zs = static_cast<size_t>(nrb) * ncb * 64;
     // Everything that does not depend on the routing facts is requested
@@ -455,24 +457,24 @@ __global__ __launch_bounds__(256) void k_split_epilogue(ApplyArgs a, const float
     // the wait counts stay exact) and the rows' h.
     RowFacts<1> f;
     row_facts_begin<1>(a, rb * 16, a.T, f);
-    f32x4_t v[MAX_TSPLIT][4];
+    f32x4_t v[MAX_TSPLIT][WC];
 #pragma unroll
     for (int z = 0; z < MAX_TSPLIT; ++z)
 #pragma unroll
-        for (int wc = 0; wc < 4; ++wc) v[z][wc] = p[min(z, splits - 1) * zs + wc * 64];
+        for (int wc = 0; wc < WC; ++wc) v[z][wc] = p[min(z, splits - 1) * zs + wc * 64];
     float hpre[2][8];
     prefetch_h1(a, rb * 16, a.T, hpre);
     row_facts_end<1>(a, rb * 16, a.T, f);
-    f32x4_t acc[1][4];
+    f32x4_t acc[1][WC];
 #pragma unroll
-    for (int wc = 0; wc < 4; ++wc) {
+    for (int wc = 0; wc < WC; ++wc) {
         acc[0][wc] = v[0][wc];
 #pragma unroll
         for (int z = 1; z < MAX_TSPLIT; ++z)
             if (z < splits) acc[0][wc] += v[z][wc];
     }
-    lora_expand_mfma<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, SEG_FUSED, f, acc, hpre);
-    store_rows<DT, 1, 4>(a, rb * 16, a.T, cb0 * 16, f, acc);
+    lora_expand_mfma<DT, 1, WC>(a, rb * 16, a.T, cb0 * 16, SEG_FUSED, f, acc, hpre);
+    store_rows<DT, 1, WC>(a, rb * 16, a.T, cb0 * 16, f, acc);
 }
 
 template <int DT, int BM, int BN>
@@ -495,8 +497,13 @@ hipError_t launch_dt(const ApplyArgs &a, float *part, hipStream_t st, LaunchEven
         LORA_LAUNCH(ev, (k_gemm_lds<DT, 128, true>), grid, dim3(512), 0, st, a, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const dim3 egrid(a.d_out / 64, (a.T + 63) / 64);
-        hipLaunchKernelGGL((k_split_epilogue<DT>), egrid, dim3(256), 0, st, a, part, splits);
+        if (a.T <= 256) {
+            const dim3 egrid(a.d_out / 32, (a.T + 63) / 64);
+            hipLaunchKernelGGL((k_split_epilogue<DT, 2>), egrid, dim3(256), 0, st, a, part, splits);
+        } else {
+            const dim3 egrid(a.d_out / 64, (a.T + 63) / 64);
+            hipLaunchKernelGGL((k_split_epilogue<DT, 4>), egrid, dim3(256), 0, st, a, part, splits);
+        }
         return hipGetLastError();
     }
     if (a.T >= 512 && a.d_out % 128 == 0) return launch_shape<DT, 128, 128>(a, st, ev);
