@@ -312,7 +312,8 @@ def cpu_baseline(w, seconds, workload):
         x, W, idx, ads = prep(lin, rows)
         reps, el = _oracle_rate(oracle, x, W, idx, w.S, ads, cores, seconds)
         value = w.T * reps / el
-        sample = "%d full calls of the %s linear (%d tokens each, fp64, %.1f s)" % (reps, lin.name, w.T, el)
+        what = "linear" if lin.name == "linear" else "%s linear" % lin.name
+        sample = "%d full calls of the %s (%d tokens each, fp64, %.1f s)" % (reps, what, w.T, el)
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "sample": sample}
 
 
