@@ -85,8 +85,10 @@ def _small_case(dtype, T, d_in, d_out, S, R, seed):
 # (T 65 .. 2047 with d_in, d_out multiples of 128; 4 and 2 splits here) and
 # the unsplit 256 x 256 tiles (T >= 2048), each with a ragged last tile; the
 # 2200- and 2300-token cases hold many adapter buckets in every 256-row tile;
-# the last two have enough 16-row bucket tiles (>= 256) for the shrink to take
-# four tiles a workgroup, with bucket boundaries inside some of the groups.
+# the 4100- and 4096-token cases have >= 256 16-row bucket tiles (one shrink
+# k part) and long and short buckets.
+# 96, 130 and 190 tokens take the split path with 64-row groups of the tile
+# wholly past T (their loads and MFMAs skipped).
 # Decode calls also cover pools beyond the epilogue's small-pool B tile (S R
 # > 1024) and beyond 64 slots (routing loads each token's slot entry; the GEMM
 # takes slots past its column groups in a second pass).
@@ -96,7 +98,9 @@ def _small_case(dtype, T, d_in, d_out, S, R, seed):
                                                (513, 64, 128, 40, 24), (200, 1024, 384, 7, 16),
                                                (1000, 512, 512, 11, 32), (2100, 256, 256, 3, 8),
                                                (2200, 256, 256, 40, 16), (2300, 512, 256, 60, 64),
-                                               (4100, 256, 256, 7, 64), (4096, 128, 128, 30, 24)])
+                                               (4100, 256, 256, 7, 64), (4096, 128, 128, 30, 24),
+                                               (96, 256, 256, 9, 16), (130, 256, 384, 12, 32),
+                                               (190, 512, 256, 5, 64)])
 @pytest.mark.parametrize("policy", [0, 1, 2])
 def test_small_ragged_full(dtype, T, d_in, d_out, S, R, policy):
     x, W, ads, idx = _small_case(dtype, T, d_in, d_out, S, R, seed=T * 31 + S)
