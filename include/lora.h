@@ -131,6 +131,9 @@ typedef struct {
  *                 LORA_BF16 both must be multiples of 64; LORA_F32 takes any.
  *   max_rank      1..LORA_MAX_RANK;  n_slots 1..LORA_MAX_SLOTS;
  *   max_tokens    >= 1.
+ * The kernels address x, W_base and y through 32-bit byte offsets: each of
+ * max_tokens*d_in, d_out*d_in and max_tokens*d_out elements must fit in
+ * 4 GiB - 1 bytes, else LORA_EINVAL.
  * Errors: LORA_EINVAL (bad sizes, out == NULL), LORA_ENOMEM, LORA_EHIP. */
 int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tokens,
                      lora_dtype dtype, lora_pool *out);
@@ -156,6 +159,11 @@ int lora_set_tenant_quota(lora_pool p, int32_t tenant, uint64_t bytes);
  *   stream  the copies are ordered after earlier work on `stream` (so A and B
  *           may have been written there) and complete before the call returns;
  *           A and B may be freed afterwards.
+ * The slot turns ACTIVE on the device after every lora_apply / lora_route /
+ * lora_plan_route enqueued on the pool before this call (on any stream) and
+ * before every one enqueued after it: each call sees the slot either FREE in
+ * all of its kernels (its tokens are invalid) or ACTIVE in all of them, never
+ * a mix.  The call does not wait for those earlier applies.
  * The slot's bytes (lora_stats.slot_bytes) are reserved against the tenant's
  * quota before anything is copied [P3 accounting]; over quota the call fails
  * with LORA_EQUOTA and nothing else changes [P1 三: never evict another].
@@ -198,7 +206,10 @@ int lora_apply(lora_pool p, const void *x, const void *W_base,
                const int32_t *token_adapter_idx, int n_tokens, void *y, void *stream);
 
 /* Routing alone, asynchronously on `stream` [P4 two-level bucketing]: the
- * per-token histogram and stable segment sort that lora_apply runs first.
+ * per-token histogram and stable segment sort, computed by the same device
+ * code lora_apply routes with for this call size (fp16/bf16 calls of at most
+ * 64 tokens route inside the decode path's epilogue; this call then runs
+ * that routing in a one-wave kernel, others the routing kernel).
  * All outputs are device int32 arrays:
  *   counts[n_slots+2]     tokens per key; key = slot, n_slots = base_only,
  *                         n_slots+1 = invalid
@@ -212,6 +223,22 @@ int lora_apply(lora_pool p, const void *x, const void *W_base,
 int lora_route(lora_pool p, const int32_t *token_adapter_idx, int n_tokens,
                int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *segs,
                int32_t *n_seg, void *stream);
+
+/* The routing the pool's kernels last used [P4 two-level bucketing; "Multi-
+ * LoRA 在线服务隔离", request identity: per-request index mapping kept intact
+ * in a mixed batch]: copies, asynchronously on `stream` (after the call that
+ * built it, also when that ran on another stream), the stable permutation and
+ * the bucket records of the last lora_apply on the pool -- or of the last
+ * lora_apply_routed of at most 64 fp16/bf16 tokens, which routes in its
+ * epilogue; a routed call of more tokens uses its plan's routing and leaves
+ * these arrays alone.
+ *   *n_tokens  host: tokens of that call (0 if no call has routed yet)
+ *   perm       device int32 [*n_tokens] (may be NULL when *n_tokens is 0)
+ *   segs       device int32 [(n_slots+2)*4], the first *n_seg records valid
+ *   n_seg      device int32 [1]
+ * Errors: LORA_EINVAL (NULL pointers), LORA_EHIP. */
+int lora_last_routing(lora_pool p, int *n_tokens, int32_t *perm, int32_t *segs, int32_t *n_seg,
+                      void *stream);
 
 /* ------------------------------------------------- route once per step -- */
 
@@ -278,7 +305,9 @@ int lora_loader_destroy(lora_loader l);
  * and errors as lora_register, nothing changes on error) and stays LOADING
  * -- tokens naming it are invalid -- until the load is committed by
  * lora_load_poll / lora_load_wait (or by a later load reusing its staging
- * buffer), which makes it ACTIVE.  When both staging buffers are in flight
+ * buffer), which makes it ACTIVE -- ordered on the device, as for
+ * lora_register, after every call already enqueued on the pool and before
+ * every later one, without waiting for them on the host.  When both staging buffers are in flight
  * the call first waits for the older one.  *ticket identifies the load.
  * The caller must wait for its loads before destroying the pool.
  * Errors: LORA_EINVAL (NULL pointers, slot out of range, adapter larger than
@@ -348,11 +377,17 @@ int lora_residency_stats_read(lora_residency r, lora_residency_stats *out);
 /* Fill *out (synchronizes with every apply enqueued on the pool). */
 int lora_pool_stats(lora_pool p, lora_stats *out);
 
-/* Bytes currently charged to `tenant` on this pool. */
+/* Bytes currently charged to `tenant` on this pool ["Multi-LoRA 在线服务隔离",
+ * memory-accounting section: resident bytes are accounted per adapter and
+ * tenant, and the release gate bounds the accounting error]: the padded slot
+ * bytes of the tenant's registered or loading slots.  Host-side; no device
+ * call.  Errors: LORA_EINVAL (NULL pointers). */
 int lora_tenant_bytes(lora_pool p, int32_t tenant, uint64_t *out);
 
-/* Read and clear the device count of invalid tokens seen by lora_apply
- * (synchronizes with every apply enqueued on the pool). */
+/* Read and clear the device count of tokens lora_apply / lora_plan_route found
+ * invalid ["Multi-LoRA 在线服务隔离", request identity: a missing mapping is an
+ * explicit error, never a fallback; their y rows are NaN].  Synchronizes with
+ * every call enqueued on the pool.  Errors: LORA_EINVAL, LORA_EHIP. */
 int lora_poll_errors(lora_pool p, uint64_t *n_invalid_tokens);
 
 /* Per-stage device time of lora_apply, for measurement.  When enabled, each

@@ -95,6 +95,18 @@ struct lora_pool_s {
     int policy = LORA_MODE_AUTO;
     int theta = kDefaultTheta;
 
+    // Slot-entry publication (register, loader commit): `gate` is recorded on
+    // `internal` after the last entry write; until it has completed, every
+    // call that reads the slot table waits for it on its own stream.
+    hipEvent_t gate = nullptr;
+    bool gate_pending = false;
+    hipEvent_t data_ev = nullptr;  // a register's copies, on the caller's stream
+
+    // The routing the pool's own arrays hold: tokens of the call that wrote
+    // it (0: none yet) and its stream (lora_last_routing).
+    int last_route_T = 0;
+    hipStream_t last_route_stream = nullptr;
+
     // Opt-in stage timing (lora_profile_enable).
     struct ProfSet {
         hipEvent_t e[7];  // stage marks 0..4; 5, 6: the base-GEMM kernel's own start / stop
@@ -164,6 +176,9 @@ void free_profile(lora_pool p) {
 
 void free_pool_memory(lora_pool p) {
     free_profile(p);
+    if (p->gate) (void)hipEventDestroy(p->gate);
+    if (p->data_ev) (void)hipEventDestroy(p->data_ev);
+    p->gate = p->data_ev = nullptr;
     if (p->A_slab) (void)hipFree(p->A_slab);
     if (p->B_slab) (void)hipFree(p->B_slab);
     if (p->slots_dev) (void)hipFree(p->slots_dev);
@@ -200,9 +215,55 @@ hipError_t drain_inflight(lora_pool p) {
 
 bool aligned(const void *ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
+// Publish slot entry `ent` so that every apply sees either the old entry in
+// all of its kernels or the new one in all of them (the decode path reads the
+// slot table in both of its launches): the write runs on the pool's internal
+// stream after every piece of work enqueued on the pool so far (and after the
+// work enqueued on `after`, which wrote the slot's slabs, when has_after), and
+// every later call that reads the slot table is ordered after it
+// (order_after_publish).  Asynchronous: nothing here waits on the host.
+// Pool mutex held, pool device current.
+hipError_t publish_entry(lora_pool p, int slot, const lora::SlotDev &ent, bool has_after, hipStream_t after) {
+    hipError_t e = hipSuccess;
+    if (has_after && after != p->internal) {
+        e = hipEventRecord(p->data_ev, after);
+        if (e == hipSuccess) e = hipStreamWaitEvent(p->internal, p->data_ev, 0);
+    }
+    for (auto &se : p->inflight)
+        if (e == hipSuccess && se.first != p->internal) e = hipStreamWaitEvent(p->internal, se.second, 0);
+    if (e == hipSuccess) e = lora::launch_set_slot(p->slots_dev, slot, ent, p->internal);
+    if (e == hipSuccess) e = hipEventRecord(p->gate, p->internal);
+    if (e == hipSuccess) {
+        p->gate_pending = true;
+        e = record_inflight(p, p->internal);
+    }
+    return e;
+}
+
+// Order the work about to be enqueued on `st` after the last slot-entry
+// publication, if it may still be in flight.
+hipError_t order_after_publish(lora_pool p, hipStream_t st) {
+    if (!p->gate_pending) return hipSuccess;
+    const hipError_t q = hipEventQuery(p->gate);
+    if (q == hipSuccess) {
+        p->gate_pending = false;
+        return hipSuccess;
+    }
+    if (q != hipErrorNotReady) return q;
+    return hipStreamWaitEvent(st, p->gate, 0);
+}
+
 }  // namespace
 
 namespace {
+
+// k splits of the decode path (two launches, routing in the epilogue) for a
+// call of n_tokens on pool p, or 0: the path of fp16/bf16 calls of 1 ..
+// DECODE_MAX_T tokens.
+int decode_splits_for(lora_pool p, int n_tokens) {
+    if (p->esz != 2 || n_tokens < 1 || n_tokens > lora::DECODE_MAX_T) return 0;
+    return lora::decode_splits(n_tokens, p->d_in);
+}
 
 // The body of lora_apply and lora_apply_routed: pool mutex held, pool device
 // current, arguments checked.  `pre`: routing already in place (a plan's), or
@@ -239,8 +300,9 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
     // threshold 0 (a bucket holds at least one token): no residual launch then.
     const bool any_separate = !(p->policy == LORA_MODE_FUSED || (p->policy == LORA_MODE_AUTO && p->theta == 0));
 
+    HIP_TRY(order_after_publish(p, st));
     HIP_TRY(mark(0));
-    const int dsplits = (half && n_tokens <= lora::DECODE_MAX_T) ? lora::decode_splits(n_tokens, p->d_in) : 0;
+    const int dsplits = decode_splits_for(p, n_tokens);
     if (dsplits > 0) {
         // Split-K GEMM with the shrink, then the epilogue, which routes,
         // sums the splits and adds the fused expand.
@@ -258,10 +320,15 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
         lora::RouteOut out = p->ro;
         if (pre) out.stats = nullptr, out.err = nullptr;
         HIP_TRY(lora::launch_decode(a, d, token_adapter_idx, out, st, kev));
+        p->last_route_T = n_tokens;
+        p->last_route_stream = st;
     } else {
-        if (!pre)
+        if (!pre) {
             HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
                                        p->ro, st));
+            p->last_route_T = n_tokens;
+            p->last_route_stream = st;
+        }
         HIP_TRY(mark(1));
         if (half) a.h_parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound);
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
@@ -320,6 +387,13 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
         default: return LORA_EINVAL;
     }
     if (esz == 2 && (d_in % 64 != 0 || d_out % 64 != 0)) return LORA_EINVAL;
+    // The kernels address x, W and y of one call through 32-bit byte offsets
+    // (buffer resources): each must stay below 4 GiB.
+    constexpr uint64_t kMaxOperand = 0xFFFFFFFFull;
+    if (static_cast<uint64_t>(max_tokens) * d_in * esz > kMaxOperand ||
+        static_cast<uint64_t>(d_out) * d_in * esz > kMaxOperand ||
+        static_cast<uint64_t>(max_tokens) * d_out * esz > kMaxOperand)
+        return LORA_EINVAL;
 
     const int Rp = (max_rank + 7) / 8 * 8;
     const uint64_t slot_bytes = static_cast<uint64_t>(Rp) * (d_in + d_out) * esz;
@@ -400,6 +474,8 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     p->device_bytes = a_bytes + b_bytes + S * sizeof(lora::SlotDev) + ws_bytes;
 
     e = hipStreamCreateWithFlags(&p->internal, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->gate, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->data_ev, hipEventDisableTiming);
     if (e == hipSuccess) e = hipMemsetAsync(p->A_slab, 0, a_bytes, p->internal);
     if (e == hipSuccess) e = hipMemsetAsync(p->B_slab, 0, b_bytes, p->internal);
     if (e == hipSuccess) e = hipMemsetAsync(p->slots_dev, 0, S * sizeof(lora::SlotDev), p->internal);
@@ -457,10 +533,11 @@ int lora_register(lora_pool p, int slot, int32_t tenant, const void *A, const vo
     hipError_t e = g.error();
     if (e == hipSuccess)
         e = lora::launch_pad_copy(A, B, p->A_slab, p->B_slab, slot, rank, p->Rp, p->d_in, p->d_out, p->esz, st);
-    lora::SlotDev ent{lora::SLOT_ACTIVE, rank, alpha / static_cast<float>(rank), 0};
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(p->slots_dev + slot, &ent, sizeof ent, hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    // The entry turns ACTIVE after the copies and after every apply already
+    // enqueued on the pool; later calls wait for it (publish_entry).
+    const lora::SlotDev ent{lora::SLOT_ACTIVE, rank, alpha / static_cast<float>(rank), 0};
+    if (e == hipSuccess) e = publish_entry(p, slot, ent, true, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);  // A and B may be freed on return
     if (e != hipSuccess) {
         p->book.abort_register(slot);
         return hip_fail(e);
@@ -542,9 +619,37 @@ int lora_route(lora_pool p, const int32_t *token_adapter_idx, int n_tokens, int3
     ro.n_seg = n_seg;
     ro.stats = nullptr;
     ro.err = nullptr;
-    HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta, ro,
-                               st));
+    HIP_TRY(order_after_publish(p, st));
+    // The routing lora_apply would run for this call: the decode epilogue's
+    // small-call routing on the decode path, the routing kernel otherwise.
+    if (decode_splits_for(p, n_tokens) > 0)
+        HIP_TRY(lora::launch_route_small(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
+                                         ro, st));
+    else
+        HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta, ro,
+                                   st));
     HIP_TRY(record_inflight(p, st));
+    return LORA_OK;
+}
+
+int lora_last_routing(lora_pool p, int *n_tokens, int32_t *perm, int32_t *segs, int32_t *n_seg, void *stream) {
+    if (p == nullptr || n_tokens == nullptr || segs == nullptr || n_seg == nullptr) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(p->mu);
+    const int T = p->last_route_T;
+    if (T > 0 && perm == nullptr) return LORA_EINVAL;
+    DeviceGuard g(p->device);
+    HIP_TRY(g.error());
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // After the call that wrote the arrays, when it ran on another stream.
+    if (T > 0 && p->last_route_stream != st)
+        for (auto &se : p->inflight)
+            if (se.first == p->last_route_stream) HIP_TRY(hipStreamWaitEvent(st, se.second, 0));
+    if (T > 0)
+        HIP_TRY(hipMemcpyAsync(perm, p->ro.perm, static_cast<size_t>(T) * 4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(segs, p->ro.segs, static_cast<size_t>(p->S + 2) * 16, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(n_seg, p->ro.n_seg, 4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(record_inflight(p, st));
+    *n_tokens = T;
     return LORA_OK;
 }
 
@@ -630,6 +735,7 @@ int lora_plan_route(lora_plan plan, lora_pool p, const int32_t *token_adapter_id
     HIP_TRY(g.error());
     hipStream_t st = static_cast<hipStream_t>(stream);
     plan->T = -1;
+    HIP_TRY(order_after_publish(p, st));
     if (n_tokens > 0) {
         HIP_TRY(hipMemcpyAsync(plan->idx, token_adapter_idx, static_cast<size_t>(n_tokens) * 4,
                                hipMemcpyDeviceToDevice, st));
@@ -713,10 +819,11 @@ int commit_load(lora_loader l, uint64_t ticket) {
     std::lock_guard<std::mutex> lk(p->mu);
     DeviceGuard g(p->device);
     hipError_t e = g.error();
-    lora::SlotDev ent{lora::SLOT_ACTIVE, pd.rank, pd.alpha / static_cast<float>(pd.rank), 0};
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(p->slots_dev + pd.slot, &ent, sizeof ent, hipMemcpyHostToDevice, p->internal);
-    if (e == hipSuccess) e = hipStreamSynchronize(p->internal);
+    // The slot's copies have completed (the caller waited for them); the
+    // entry turns ACTIVE after every apply already enqueued on the pool, and
+    // later calls wait for it.  Nothing here blocks (lora_load_poll).
+    const lora::SlotDev ent{lora::SLOT_ACTIVE, pd.rank, pd.alpha / static_cast<float>(pd.rank), 0};
+    if (e == hipSuccess) e = publish_entry(p, pd.slot, ent, false, nullptr);
     if (e != hipSuccess) {
         p->book.abort_register(pd.slot);
         return hip_fail(e);

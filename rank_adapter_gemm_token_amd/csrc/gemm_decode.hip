@@ -215,6 +215,35 @@ __device__ __forceinline__ void publish_route(const SmallRoute &sr, int T, const
     }
 }
 
+// Routing alone of a call of 1 .. 64 tokens (lora_route on an fp16/bf16
+// pool): the small_route that the decode epilogue runs, published the same
+// way, plus the per-key counts and offsets the epilogue has no use for.  One
+// wave.  A key's count is the length of its bucket (0 without one); its
+// offset is where the first bucket of a key not below it starts (T past the
+// last), i.e. the exclusive prefix sum of the counts.
+__global__ __launch_bounds__(64) void k_route_small(const int32_t *__restrict__ idx, int T, int S,
+                                                    const SlotDev *__restrict__ slots, int max_rank, int policy,
+                                                    int theta, RouteOut out) {
+    __shared__ SmallRoute sr;
+    const int lane = threadIdx.x & 63;
+    const int v = lane < T ? idx[lane] : -1;
+    const int2 e = reinterpret_cast<const int2 *>(slots)[2 * min(max(v, 0), S - 1)];
+    small_route(v, e.x, e.y, T, S, max_rank, policy, theta, sr);
+    lds_fence();
+    publish_route(sr, T, out);
+    const int ns = sr.n_seg;
+    for (int k = lane; k < S + 3; k += 64) {
+        int lo = 0, hi = ns;  // first record whose key is >= k
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sr.segs[mid][0] < k) lo = mid + 1;
+            else hi = mid;
+        }
+        out.offsets[k] = lo < ns ? sr.segs[lo][1] : T;
+        if (k < S + 2) out.counts[k] = (lo < ns && sr.segs[lo][0] == k) ? sr.segs[lo][2] : 0;
+    }
+}
+
 // ------------------------------------------------------------------ GEMM --
 
 using lds_ptr = __attribute__((address_space(3))) void *;
@@ -701,6 +730,13 @@ hipError_t launch_decode(const ApplyArgs &a, const DecodeArgs &d, const int32_t 
                          hipStream_t st, LaunchEvents ev) {
     return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, d, idx, out, st, ev)
                                : launch_dt<DT_BF16>(a, d, idx, out, st, ev);
+}
+
+hipError_t launch_route_small(const int32_t *idx, int T, int S, const SlotDev *slots, int max_rank, int policy,
+                              int theta, const RouteOut &out, hipStream_t st) {
+    if (T < 1 || T > DECODE_MAX_T) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(64), 0, st, idx, T, S, slots, max_rank, policy, theta, out);
+    return hipGetLastError();
 }
 
 }  // namespace lora

@@ -88,6 +88,9 @@ hipError_t launch_pad_copy(const void *A_user, const void *B_user, void *A_slab,
                            int slot, int rank, int R, int d_in, int d_out, int esz,
                            hipStream_t st);
 
+// Write slot-table entry `slot` (one thread, on stream st).
+hipError_t launch_set_slot(SlotDev *slots, int slot, SlotDev ent, hipStream_t st);
+
 struct ApplyArgs {
     int dtype;          // lora_dtype
     int T, d_in, d_out, S;
@@ -144,6 +147,11 @@ struct DecodeArgs {
 // ev (optional) times the GEMM launch.
 hipError_t launch_decode(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,
                          hipStream_t st, LaunchEvents ev = {});
+// The decode epilogue's routing alone (1 <= T <= DECODE_MAX_T): writes every
+// array of `out` that launch_route writes, counts and offsets included, and
+// the same values (both are the stable counting sort of the keys).
+hipError_t launch_route_small(const int32_t *idx, int T, int S, const SlotDev *slots, int max_rank, int policy,
+                              int theta, const RouteOut &out, hipStream_t st);
 // k splits of the decode GEMM for (T, d_in); 0 if d_in is too large for it.
 int decode_splits(int T, int d_in);
 int decode_token_blocks(int T);

@@ -36,7 +36,18 @@ __global__ __launch_bounds__(256) void k_pad_copy(const E *__restrict__ A_user,
     }
 }
 
+// One slot-table entry, written by a kernel on the pool's internal stream so
+// that the write is ordered by stream events like any other pool work.
+__global__ void k_set_slot(SlotDev *slots, int slot, SlotDev ent) {
+    if (threadIdx.x == 0) slots[slot] = ent;
+}
+
 }  // namespace
+
+hipError_t launch_set_slot(SlotDev *slots, int slot, SlotDev ent, hipStream_t st) {
+    hipLaunchKernelGGL(k_set_slot, dim3(1), dim3(64), 0, st, slots, slot, ent);
+    return hipGetLastError();
+}
 
 hipError_t launch_pad_copy(const void *A_user, const void *B_user, void *A_slab, void *B_slab,
                            int slot, int rank, int R, int d_in, int d_out, int esz,

@@ -41,7 +41,7 @@ TORCH_DTYPE = {v: k for k, v in DTYPE_OF.items()}
 
 # Every symbol include/lora.h declares, in declaration order.
 EXPORTS = ["lora_pool_create", "lora_pool_destroy", "lora_set_tenant_quota", "lora_register",
-           "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_route",
+           "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_route", "lora_last_routing",
            "lora_plan_create", "lora_plan_destroy", "lora_plan_route", "lora_apply_routed",
            "lora_loader_create", "lora_loader_destroy", "lora_load_async", "lora_load_poll", "lora_load_wait",
            "lora_residency_create", "lora_residency_destroy", "lora_residency_set_share",
@@ -85,6 +85,7 @@ _lib.lora_set_policy.argtypes = [_vp, _i, _i]
 _lib.lora_get_policy.argtypes = [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i)]
 _lib.lora_apply.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
 _lib.lora_route.argtypes = [_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.lora_last_routing.argtypes = [_vp, ctypes.POINTER(_i), _vp, _vp, _vp, _vp]
 _lib.lora_plan_create.argtypes = [_i, _i, ctypes.POINTER(_vp)]
 _lib.lora_plan_destroy.argtypes = [_vp]
 _lib.lora_plan_route.argtypes = [_vp, _vp, _vp, _i, _vp]
@@ -235,6 +236,20 @@ def lora_route(pool, token_adapter_idx, n_tokens, counts, offsets, perm, segs, n
         _need(n_seg, 1, torch.int32, "n_seg")
     _check(_lib.lora_route(pool, _ptr(token_adapter_idx), int(n_tokens), _ptr(counts), _ptr(offsets),
                            _ptr(perm), _ptr(segs), _ptr(n_seg), _stream(stream)), "lora_route")
+
+
+def lora_last_routing(pool, perm, segs, n_seg, stream=None):
+    """Copies the routing the pool's kernels last used into perm / segs / n_seg
+    (device int32 tensors); returns that call's token count."""
+    sh = _shapes.get(pool)
+    if sh is not None:
+        _need(segs, (sh["S"] + 2) * 4, torch.int32, "segs")
+        _need(n_seg, 1, torch.int32, "n_seg")
+        _need(perm, 0, torch.int32, "perm")  # the call's token count is known after it
+    n = _i()
+    _check(_lib.lora_last_routing(pool, ctypes.byref(n), _ptr(perm), _ptr(segs), _ptr(n_seg), _stream(stream)),
+           "lora_last_routing")
+    return n.value
 
 
 # Plans created through this binding: capacity and the last routed batch size.

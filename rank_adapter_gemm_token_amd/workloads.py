@@ -180,19 +180,23 @@ def stack_x(d_in, seed=5, T=256, device="cpu"):
 
 
 def stack_linear(layer, proj, device, seed=5, S=64, r=16) -> Linear:
-    """One linear of the 7B stack, drawn on `device` with a seeded torch generator."""
+    """One linear of the 7B stack, drawn on `device` with a seeded torch generator.
+
+    Three draws per linear (W, then every adapter's A at once, then every B):
+    a few large dispatches rather than one pair per adapter, which keeps the
+    set-up of the 224-linear stack to a few hundred device dispatches."""
     name, d_in, d_out = STACK_SHAPES[proj]
     g = torch.Generator(device=device)
     g.manual_seed(1000 * seed + 8 * layer + proj)
 
     def randn(shape, var):
         t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-        return (t * float(np.sqrt(var))).to(torch.bfloat16)
+        return t.mul_(float(np.sqrt(var))).to(torch.bfloat16)
 
     W = randn((d_out, d_in), 1.0 / d_in)
-    ad = [Adapter(slot=i, tenant=i, rank=r, alpha=2.0 * r,
-                  A=randn((r, d_in), 1.0 / d_in), B=randn((d_out, r), 0.01))
-          for i in range(S)]
+    A_all = randn((S, r, d_in), 1.0 / d_in)
+    B_all = randn((S, d_out, r), 0.01)
+    ad = [Adapter(slot=i, tenant=i, rank=r, alpha=2.0 * r, A=A_all[i], B=B_all[i]) for i in range(S)]
     return Linear("layer%d.%s" % (layer, name), d_in, d_out, W, ad)
 
 

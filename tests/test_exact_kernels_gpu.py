@@ -1,0 +1,211 @@
+"""The exact properties the pages fix, on every base-GEMM kernel of lora_apply.
+
+Each shape below is chosen so that the library takes one kernel (the variant
+depends on (T, d_in, d_out, dtype) only):
+
+  decode64    k_decode_gemm, 4 token blocks, + k_decode_epilogue (T <= 64)
+  decode5     the same with 1 token block
+  decodeS70   the same, 70 slots over 4 column groups (second shrink pass)
+  split_wc2   k_gemm_lds<128, split> + k_split_epilogue, 32-column waves
+              (65 .. 256 tokens), 4 k splits, a 64-row x group past T
+  split_wc4   the same with 64-column waves (257 .. 2047 tokens), two
+              256-row tiles
+  big         k_gemm_lds<256> (>= 2048 tokens, 256-row tiles)
+  tiled       k_gemm_tiled (shapes off the 128 grid)
+
+Properties (each exact, compared as values; NaN rows compare equal):
+  * base_only rows equal the rows of an all-base_only call ("xpshop.cn
+    article 492", section 三: routing default base_only, the base is shared);
+  * permuting the batch permutes the rows ("Multi-LoRA 在线服务隔离", request
+    identity section: per-request index mapping in a mixed batch);
+  * a token's row does not change when every other token changes adapter,
+    under a forced mode (same section: no cross-tenant bleed; release-gate
+    section: zero attribution errors);
+  * an adapter whose B is zero is a no-op ("LLM 多 LoRA 推理服务工程 2026",
+    four-layer runtime, execution-unit paragraph: the LoRA product is a
+    residual added to the base);
+  * repeated calls are bitwise identical;
+  * small-integer inputs give exactly the oracle's values (every partial sum
+    is an integer the accumulator and the pool dtype hold exactly, so any
+    correct summation order, fused or separate, must agree).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import Pool, assert_close, dev, reference
+from rank_adapter_gemm_token_amd import lora
+from rank_adapter_gemm_token_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+# name -> (T, d_in, d_out, S, R)
+SHAPES = {
+    "decode64": (64, 4096, 1024, 6, 16),
+    "decode5": (5, 2048, 256, 4, 16),
+    "decodeS70": (64, 512, 256, 70, 16),
+    "split_wc2": (130, 1024, 256, 9, 16),
+    "split_wc4": (300, 1024, 512, 9, 32),
+    "big": (2048, 256, 256, 12, 64),
+    "tiled": (70, 128, 192, 6, 16),
+}
+TDT = {"f16": torch.float16, "bf16": torch.bfloat16}
+POLICIES = [lora.LORA_MODE_AUTO, lora.LORA_MODE_FUSED, lora.LORA_MODE_SEPARATE]
+FORCED = [lora.LORA_MODE_FUSED, lora.LORA_MODE_SEPARATE]
+
+
+def _same(a, b):
+    """Equal as values, NaN == NaN (invalid rows are all NaN)."""
+    a, b = a.float(), b.float()
+    return bool(((a == b) | (torch.isnan(a) & torch.isnan(b))).all())
+
+
+def _normal_case(shape, dtype, seed):
+    T, d_in, d_out, S, R = SHAPES[shape]
+    rng = np.random.default_rng(seed)
+    tdt = TDT[dtype]
+    x = torch.from_numpy(rng.standard_normal((T, d_in))).to(tdt)
+    W = torch.from_numpy(rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).to(tdt)
+    ads = []
+    for s in range(S):
+        r = int(rng.integers(1, R + 1))
+        ads.append(wl.Adapter(s, s, r, float(2 * r),
+                              torch.from_numpy(rng.standard_normal((r, d_in)) / np.sqrt(d_in)).to(tdt),
+                              torch.from_numpy(rng.standard_normal((d_out, r)) * 0.1).to(tdt)))
+    # Every slot, base_only and a few invalid indices.
+    idx = rng.integers(-1, S, size=T)
+    idx[rng.random(T) < 0.03] = S + 3
+    return x, W, ads, torch.from_numpy(idx.astype(np.int32))
+
+
+def _pool(shape, dtype, policy, ads, theta=16):
+    T, d_in, d_out, S, R = SHAPES[shape]
+    p = Pool(d_in, d_out, R, S, T, dtype, policy, theta)
+    p.register_all(ads)
+    return p
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("policy", POLICIES)
+def test_base_only_rows_exact(shape, policy):
+    x, W, ads, idx = _normal_case(shape, "bf16", 1)
+    p = _pool(shape, "bf16", policy, ads)
+    try:
+        y_mixed = p.apply(dev(x), dev(W), dev(idx)).cpu()
+        y_base = p.apply(dev(x), dev(W), dev(torch.full_like(idx, -1))).cpu()
+        b = (idx == -1).numpy()
+        assert b.any()
+        assert _same(y_mixed[b], y_base[b])
+        ref, inv = reference(p, x, W, torch.full_like(idx, -1))
+        assert_close(y_base, ref, inv, "bf16")
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("policy", POLICIES)
+def test_batch_order_invariance(shape, policy):
+    x, W, ads, idx = _normal_case(shape, "f16", 2)
+    p = _pool(shape, "f16", policy, ads)
+    try:
+        perm = torch.from_numpy(np.random.default_rng(3).permutation(idx.numel()))
+        y = p.apply(dev(x), dev(W), dev(idx)).cpu()
+        yp = p.apply(dev(x[perm]), dev(W), dev(idx[perm])).cpu()
+        assert _same(yp, y[perm])
+        ref, inv = reference(p, x, W, idx)
+        assert_close(y, ref, inv, "f16")
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("policy", FORCED)
+def test_no_cross_tenant_bleed(shape, policy):
+    T, d_in, d_out, S, R = SHAPES[shape]
+    x, W, ads, idx = _normal_case(shape, "bf16", 4)
+    p = _pool(shape, "bf16", policy, ads)
+    try:
+        y0 = p.apply(dev(x), dev(W), dev(idx)).cpu()
+        rng = np.random.default_rng(11)
+        for trial in range(3):
+            other = torch.from_numpy(rng.integers(-1, S + 1, size=T).astype(np.int32))
+            keep = torch.from_numpy(rng.random(T) < 0.25)
+            mixed = torch.where(keep, idx, other)
+            y1 = p.apply(dev(x), dev(W), dev(mixed)).cpu()
+            assert _same(y1[keep], y0[keep])
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("policy", POLICIES)
+def test_zero_B_is_noop(shape, policy):
+    x, W, ads, idx = _normal_case(shape, "f16", 5)
+    a = ads[1]
+    ads[1] = wl.Adapter(a.slot, a.tenant, a.rank, a.alpha, a.A, torch.zeros_like(a.B))
+    p = _pool(shape, "f16", policy, ads)
+    try:
+        one = torch.full_like(idx, 1)
+        y = p.apply(dev(x), dev(W), dev(one)).cpu()
+        y_base = p.apply(dev(x), dev(W), dev(torch.full_like(idx, -1))).cpu()
+        assert _same(y, y_base)
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_repeat_calls_bitwise(shape):
+    x, W, ads, idx = _normal_case(shape, "bf16", 6)
+    p = _pool(shape, "bf16", lora.LORA_MODE_AUTO, ads, theta=0)
+    try:
+        xd, Wd, idd = dev(x), dev(W), dev(idx)
+        first = p.apply(xd, Wd, idd).cpu().view(torch.int16)
+        for _ in range(5):
+            assert torch.equal(p.apply(xd, Wd, idd).cpu().view(torch.int16), first)
+    finally:
+        p.close()
+
+
+def _integer_case(shape, dtype, seed):
+    """x in {-1, 0, 1} (fp16: {-2 .. 2}), sparse +-1 W, A and B, true ranks
+    of 1 .. 16 with alpha / rank in {1, 2}: every product and partial sum is
+    a small integer."""
+    T, d_in, d_out, S, R = SHAPES[shape]
+    rng = np.random.default_rng(seed)
+    tdt = TDT[dtype]
+    amp = 2 if dtype == "f16" else 1
+    dens = min(0.25, 24.0 / d_in)
+    x = rng.integers(-amp, amp + 1, size=(T, d_in))
+    W = (rng.random((d_out, d_in)) < dens) * rng.integers(-1, 2, size=(d_out, d_in))
+    ads = []
+    for s in range(S):
+        rk = int(rng.choice([r for r in (1, 2, 4, 8, 16) if r <= R]))
+        A = (rng.random((rk, d_in)) < dens) * rng.integers(-1, 2, size=(rk, d_in))
+        B = (rng.random((d_out, rk)) < 0.15) * rng.integers(-1, 2, size=(d_out, rk))
+        alpha = float(rk * int(rng.integers(1, 3)))
+        ads.append(wl.Adapter(s, s, rk, alpha, torch.from_numpy(A).to(tdt), torch.from_numpy(B).to(tdt)))
+    idx = torch.from_numpy(rng.integers(-1, S, size=T).astype(np.int32))
+    return torch.from_numpy(x).to(tdt), torch.from_numpy(W).to(tdt), ads, idx
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("dtype,limit", [("f16", 2048), ("bf16", 256)])
+@pytest.mark.parametrize("policy", POLICIES)
+def test_integer_inputs_exact(shape, dtype, limit, policy):
+    x, W, ads, idx = _integer_case(shape, dtype, 7)
+    # The scaled h (an MFMA operand in the pool dtype on the tiled paths) and
+    # every output stay within the dtype's exact-integer range.
+    xs = x.double().numpy()
+    for a in ads:
+        h = (a.alpha / a.rank) * (xs @ a.A.double().numpy().T)
+        assert np.abs(h).max() <= limit
+    p = _pool(shape, dtype, policy, ads, theta=8)
+    try:
+        y = p.apply(dev(x), dev(W), dev(idx)).cpu()
+        ref, inv = reference(p, x, W, idx)
+        assert not inv.any()
+        assert np.abs(ref).max() <= limit
+        assert np.array_equal(oracle.to_f64(y), ref)
+    finally:
+        p.close()

@@ -69,6 +69,12 @@ def test_validation_before_device_use():
     assert lib.lora_pool_create(64, 64, 8, 4, 16, 7, ctypes.byref(h)) == L.LORA_EINVAL
     assert lib.lora_pool_create(96, 64, 8, 4, 16, 1, ctypes.byref(h)) == L.LORA_EINVAL  # fp16 needs %64
     assert lib.lora_pool_create(64, 64, 8, 4, 16, 1, None) == L.LORA_EINVAL
+    # x, W or y of 4 GiB or more: the kernels' 32-bit byte offsets could not reach them.
+    assert lib.lora_pool_create(65536, 32768, 8, 4, 16, 1, ctypes.byref(h)) == L.LORA_EINVAL  # W 4 GiB
+    assert lib.lora_pool_create(4096, 64, 8, 4, 524288, 1, ctypes.byref(h)) == L.LORA_EINVAL  # x 4 GiB
+    assert lib.lora_pool_create(64, 4096, 8, 4, 524288, 1, ctypes.byref(h)) == L.LORA_EINVAL  # y 4 GiB
+    assert lib.lora_pool_create(32768, 32768, 8, 4, 16, 0, ctypes.byref(h)) == L.LORA_EINVAL  # fp32 W 4 GiB
+    assert lib.lora_last_routing(None, None, None, None, None, None) == L.LORA_EINVAL
     # Null pool handles.
     assert lib.lora_pool_destroy(None) == L.LORA_OK
     assert lib.lora_apply(None, None, None, None, 4, None, None) == L.LORA_EINVAL

@@ -1,24 +1,55 @@
-"""Routing on the GPU (lora_route through the C ABI) vs the oracle: every array
-bit-exact -- counts, offsets, the stable permutation and the bucket records."""
+"""Routing on the GPU vs the oracle: every array bit-exact -- counts, offsets,
+the stable permutation and the bucket records.
+
+Two routing implementations run on the device: the routing kernel (calls of
+more than 64 tokens, and fp32 pools) and the small-call routing inside the
+decode epilogue (fp16/bf16 calls of at most 64 tokens).  lora_route runs the
+one lora_apply would run for the call, so the cases below cover both: fp16
+pools at T <= 64 take the small-call routing, fp32 pools and T > 64 the
+routing kernel.  lora_last_routing reads back what lora_apply's own kernels
+built, which is compared too."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from gpu_helpers import Pool, dev
+from rank_adapter_gemm_token_amd import lora
 from rank_adapter_gemm_token_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
 
-def _pool_with_slots(S, active, max_T, policy=0, theta=16):
-    p = Pool(64, 64, 8, S, max_T, "f16", policy=policy, theta=theta)
+def _pool_with_slots(S, active, max_T, policy=0, theta=16, dtype="f16"):
+    p = Pool(64, 64, 8, S, max_T, dtype, policy=policy, theta=theta)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
     g = torch.Generator().manual_seed(S)
     for s in np.flatnonzero(active):
-        A = torch.randn((4, 64), generator=g).to(torch.float16)
-        B = torch.randn((64, 4), generator=g).to(torch.float16)
+        A = torch.randn((4, 64), generator=g).to(tdt)
+        B = torch.randn((64, 4), generator=g).to(tdt)
         p.register(int(s), A, B, 4, 8.0)
     return p
+
+
+def _compare_applied(p, idx_np, active, policy=0, theta=16):
+    """lora_apply's own routing (read back with lora_last_routing) vs the oracle."""
+    T = len(idx_np)
+    idx = dev(torch.from_numpy(np.asarray(idx_np, np.int32)))
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[p.dtype]
+    x = torch.zeros((T, p.d_in), dtype=tdt, device="cuda")
+    W = torch.zeros((p.d_out, p.d_in), dtype=tdt, device="cuda")
+    p.apply(x, W, idx)
+    perm = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+    segs = torch.full(((p.S + 2) * 4,), -7, dtype=torch.int32, device="cuda")
+    n_seg = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    n = lora.lora_last_routing(p.h, perm, segs, n_seg)
+    torch.cuda.synchronize()
+    assert n == T
+    ref = oracle.route(idx_np, p.S, active, policy, theta)
+    k = int(n_seg.item())
+    assert k == ref["n_seg"]
+    assert perm.cpu().numpy().tolist() == ref["perm"].tolist()
+    assert segs.cpu().numpy().reshape(p.S + 2, 4)[:k].tolist() == ref["segs"].tolist()
 
 
 def _compare(p, idx_np, active, policy=0, theta=16):
@@ -43,12 +74,15 @@ def _edge(T, S, rng):
     }
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 1023, 1024, 1025, 3001, 4096])
-def test_route_edge_cases(T):
+# fp16 pools route calls of at most 64 tokens with the small-call routing,
+# fp32 pools always with the routing kernel.
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("T", [1, 2, 17, 63, 64, 65, 1023, 1024, 1025, 3001, 4096])
+def test_route_edge_cases(T, dtype):
     S = 12
     active = np.ones(S, np.int32)
     active[[3, 7]] = 0  # registered nowhere: tokens naming them are invalid
-    p = _pool_with_slots(S, active, 4096)
+    p = _pool_with_slots(S, active, 4096, dtype=dtype)
     try:
         rng = np.random.default_rng(T)
         for name, idx in _edge(T, S, rng).items():
@@ -57,14 +91,72 @@ def test_route_edge_cases(T):
         p.close()
 
 
+# What lora_apply itself routed with: the decode epilogue (fp16/bf16, T <= 64)
+# and the routing kernel (more tokens), under every policy.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T", [1, 2, 33, 63, 64, 65, 300])
+@pytest.mark.parametrize("policy,theta", [(0, 0), (0, 3), (1, 16), (2, 16)])
+def test_applied_routing_bit_exact(T, dtype, policy, theta):
+    S = 12
+    active = np.ones(S, np.int32)
+    active[[3, 7]] = 0
+    p = _pool_with_slots(S, active, 512, policy, theta, dtype=dtype)
+    try:
+        rng = np.random.default_rng(T + 1000 * policy + theta)
+        for name, idx in _edge(T, S, rng).items():
+            _compare_applied(p, idx, active, policy, theta)
+        _compare_applied(p, rng.integers(-1, S, size=T), active, policy, theta)
+    finally:
+        p.close()
+
+
+def test_applied_routing_workloads():
+    # The decode and sweep workloads' own index arrays, through lora_apply.
+    cases = [("decode", wl.decode().idx, 6)] + [("sweep%d" % T, wl.sweep(T).idx, 100) for T in wl.SWEEP_T]
+    for name, idx, S in cases:
+        active = np.ones(S, np.int32)
+        p = _pool_with_slots(S, active, 64, 0, 0)
+        try:
+            _compare_applied(p, idx.numpy(), active, 0, 0)
+        finally:
+            p.close()
+
+
+def test_applied_routing_max_slots():
+    # 1024 slots, half registered: keys up to 1025 on the small-call routing.
+    S = 1024
+    rng = np.random.default_rng(6)
+    active = (rng.random(S) < 0.5).astype(np.int32)
+    p = _pool_with_slots(S, active, 64)
+    try:
+        for T in (1, 64):
+            _compare_applied(p, rng.integers(-1, S + 2, size=T), active)
+            _compare(p, rng.integers(-1, S + 2, size=T), active)
+    finally:
+        p.close()
+
+
+def test_last_routing_before_any_call():
+    p = _pool_with_slots(4, np.ones(4, np.int32), 16)
+    try:
+        segs = torch.full((6 * 4,), -7, dtype=torch.int32, device="cuda")
+        n_seg = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        assert lora.lora_last_routing(p.h, None, segs, n_seg) == 0
+        torch.cuda.synchronize()
+        assert int(n_seg.item()) == 0
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("T", [60, 500])
 @pytest.mark.parametrize("policy,theta", [(0, 0), (0, 3), (0, 16), (0, 1000), (1, 16), (2, 16)])
-def test_route_policies(policy, theta):
+def test_route_policies(policy, theta, T):
     S = 20
     active = np.ones(S, np.int32)
     p = _pool_with_slots(S, active, 512, policy, theta)
     try:
         rng = np.random.default_rng(99)
-        idx = rng.choice(np.arange(-1, S), size=500, p=None)
+        idx = rng.choice(np.arange(-1, S), size=T, p=None)
         _compare(p, idx, active, policy, theta)
     finally:
         p.close()
