@@ -97,6 +97,11 @@ typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_FUSED = 1, LORA_MODE_SEPARATE = 2 }
 #define LORA_ENOMEM (-9)      /* device or host allocation failed */
 #define LORA_EHIP (-10)       /* a HIP runtime call failed; lora_strerror has no detail,
                                  lora_last_hip_error() has the HIP text */
+#define LORA_ESCRATCH (-11)   /* lora_apply_noalloc: the call's workspace exceeds
+                                 LORA_NOALLOC_SCRATCH_BYTES */
+
+/* Size of the library's static per-device workspace (lora_apply_noalloc). */
+#define LORA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Pool statistics.  The `last_*` fields describe the most recent lora_apply
  * on the pool and are read back from the device (lora_pool_stats
@@ -204,6 +209,27 @@ int lora_get_policy(lora_pool p, lora_mode *mode, int *threshold);
  * Errors (host-side, nothing enqueued): LORA_EINVAL, LORA_ETOKENS, LORA_EHIP. */
 int lora_apply(lora_pool p, const void *x, const void *W_base,
                const int32_t *token_adapter_idx, int n_tokens, void *y, void *stream);
+
+/* lora_apply for callers that cannot allocate device memory at call time
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same result, bit for bit, but the
+ * call's workspace (routing arrays, h parts, split-K partial sums) lives in
+ * the library's static per-device array of LORA_NOALLOC_SCRATCH_BYTES,
+ * resolved when the first pool was created on the device; the call allocates
+ * nothing and creates no HIP object.  Arguments, ordering and errors as
+ * lora_apply, plus LORA_ESCRATCH (nothing enqueued) when the call needs more
+ * workspace than the array holds: about 4 * splits * T * d_out bytes of
+ * split-K partial sums plus the routing arrays and h -- every 7B-shaped
+ * projection fits at up to 64 tokens, 4096-wide ones at up to 192, calls of
+ * 2048 tokens and more (no split) at any width.  The array is shared by every pool and stream of the
+ * device: two lora_apply_noalloc calls that may overlap in time race, so the
+ * caller orders them (one stream, or events).  Nothing in it needs to start
+ * at zero (every word a kernel reads was written earlier in the same call).
+ * The pool's own workspace, the routing lora_last_routing reads and the
+ * statistics are unaffected, except the last-call statistics and the error
+ * counter, which the call updates as lora_apply does. */
+int lora_apply_noalloc(lora_pool p, const void *x, const void *W_base,
+                       const int32_t *token_adapter_idx, int n_tokens, void *y, void *stream);
 
 /* Routing alone, asynchronously on `stream` [P4 two-level bucketing]: the
  * per-token histogram and stable segment sort, computed by the same device

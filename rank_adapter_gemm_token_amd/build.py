@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "ledger.cpp", "residency.cpp", "route.hip", "pad_copy.hip", "apply_kernels.hip", "gemm_decode.hip",
-           "gemm_tiled.hip", "shrink_expand.hip"]
+           "gemm_tiled.hip", "shrink_expand.hip", "scratch.hip"]
 
 # Packed-fp32 VALU instructions are kept out of every device object.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -101,6 +101,10 @@ struct lora_pool_s {
     hipEvent_t gate = nullptr;
     bool gate_pending = false;
     hipEvent_t data_ev = nullptr;  // a register's copies, on the caller's stream
+    // Completion of the last lora_apply_noalloc (created with the pool: that
+    // call creates nothing); drains wait for it too once it has been recorded.
+    hipEvent_t noalloc_done = nullptr;
+    bool noalloc_used = false;
 
     // The routing the pool's own arrays hold: tokens of the call that wrote
     // it (0: none yet) and its stream (lora_last_routing).
@@ -178,7 +182,8 @@ void free_pool_memory(lora_pool p) {
     free_profile(p);
     if (p->gate) (void)hipEventDestroy(p->gate);
     if (p->data_ev) (void)hipEventDestroy(p->data_ev);
-    p->gate = p->data_ev = nullptr;
+    if (p->noalloc_done) (void)hipEventDestroy(p->noalloc_done);
+    p->gate = p->data_ev = p->noalloc_done = nullptr;
     if (p->A_slab) (void)hipFree(p->A_slab);
     if (p->B_slab) (void)hipFree(p->B_slab);
     if (p->slots_dev) (void)hipFree(p->slots_dev);
@@ -210,6 +215,7 @@ hipError_t drain_inflight(lora_pool p) {
         hipError_t e = hipEventSynchronize(se.second);
         if (e != hipSuccess) return e;
     }
+    if (p->noalloc_used) return hipEventSynchronize(p->noalloc_done);
     return hipSuccess;
 }
 
@@ -231,6 +237,7 @@ hipError_t publish_entry(lora_pool p, int slot, const lora::SlotDev &ent, bool h
     }
     for (auto &se : p->inflight)
         if (e == hipSuccess && se.first != p->internal) e = hipStreamWaitEvent(p->internal, se.second, 0);
+    if (e == hipSuccess && p->noalloc_used) e = hipStreamWaitEvent(p->internal, p->noalloc_done, 0);
     if (e == hipSuccess) e = lora::launch_set_slot(p->slots_dev, slot, ent, p->internal);
     if (e == hipSuccess) e = hipEventRecord(p->gate, p->internal);
     if (e == hipSuccess) {
@@ -265,11 +272,72 @@ int decode_splits_for(lora_pool p, int n_tokens) {
     return lora::decode_splits(n_tokens, p->d_in);
 }
 
+// The device workspace one call's kernels use: the routing arrays (stats and
+// the error counter are always the pool's), h and the split-K partial sums.
+struct CallSpace {
+    lora::RouteOut ro;
+    float *h;
+    float *part;
+};
+
+// Lay out the workspace of one call of n_tokens (>= 1) on pool p from `base`
+// (256-byte aligned pieces, sized for this call only) and return its bytes;
+// base == nullptr only measures.
+size_t carve_call(lora_pool p, int n_tokens, char *base, CallSpace *cs) {
+    const size_t T = static_cast<size_t>(n_tokens), S = static_cast<size_t>(p->S);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const size_t o_counts = take((S + 2) * 4);
+    const size_t o_offsets = take((S + 3) * 4);
+    const size_t o_perm = take(T * 4);
+    const size_t o_segs = take((S + 2) * 16);
+    const size_t o_nseg = take(4);
+    const size_t o_posseg = take(T * 4);
+    const size_t o_tokpos = take(T * 4);
+    const size_t o_tokseg = take(T * 4);
+    const size_t o_tiles = take(static_cast<size_t>(lora::max_tiles(n_tokens, p->S)) * 8);
+    const size_t o_ntiles = take(4);
+    // h parts and partial sums, as the launchers lay them out for this call.
+    const int dsplits = decode_splits_for(p, n_tokens);
+    size_t h_parts = 1, part_floats = 0;
+    if (dsplits > 0) {
+        h_parts = static_cast<size_t>(dsplits);
+        part_floats = static_cast<size_t>(dsplits) * lora::decode_token_blocks(n_tokens) * 16 * p->d_out;
+    } else if (p->esz == 2) {
+        h_parts = static_cast<size_t>(lora::tiled_h_parts(p->d_in, p->Rp, lora::max_tiles(n_tokens, p->S)));
+        part_floats = static_cast<size_t>(lora::tiled_splits(n_tokens, p->d_in, p->d_out)) * ((T + 15) / 16 * 16) *
+                      p->d_out;
+    }
+    const size_t o_h = take(h_parts * T * p->Rp * 4);
+    const size_t o_part = take(part_floats * 4);
+    if (base != nullptr) {
+        cs->ro.counts = reinterpret_cast<int32_t *>(base + o_counts);
+        cs->ro.offsets = reinterpret_cast<int32_t *>(base + o_offsets);
+        cs->ro.perm = reinterpret_cast<int32_t *>(base + o_perm);
+        cs->ro.segs = reinterpret_cast<int32_t *>(base + o_segs);
+        cs->ro.n_seg = reinterpret_cast<int32_t *>(base + o_nseg);
+        cs->ro.pos_seg = reinterpret_cast<int32_t *>(base + o_posseg);
+        cs->ro.tok_pos = reinterpret_cast<int32_t *>(base + o_tokpos);
+        cs->ro.tok_seg = reinterpret_cast<int32_t *>(base + o_tokseg);
+        cs->ro.tiles = reinterpret_cast<int32_t *>(base + o_tiles);
+        cs->ro.n_tiles = reinterpret_cast<int32_t *>(base + o_ntiles);
+        cs->ro.stats = p->ro.stats;
+        cs->ro.err = p->ro.err;
+        cs->h = reinterpret_cast<float *>(base + o_h);
+        cs->part = reinterpret_cast<float *>(base + o_part);
+    }
+    return off;
+}
+
 // The body of lora_apply and lora_apply_routed: pool mutex held, pool device
 // current, arguments checked.  `pre`: routing already in place (a plan's), or
 // nullptr to route here.
 int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *token_adapter_idx, int n_tokens,
-                 void *y, hipStream_t st, const lora::RouteOut *pre) {
+                 void *y, hipStream_t st, const lora::RouteOut *pre, const CallSpace &cs, bool noalloc) {
     lora_pool_s::ProfSet *ps = (p->prof_used < p->prof.size()) ? &p->prof[p->prof_used++] : nullptr;
     auto mark = [&](int i) { return ps ? hipEventRecord(ps->e[i], st) : hipSuccess; };
     lora::LaunchEvents kev{};
@@ -288,10 +356,10 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
     a.A_slab = p->A_slab;
     a.B_slab = p->B_slab;
     a.slots = p->slots_dev;
-    a.h = p->h;
+    a.h = cs.h;
     a.h_parts = 1;
     // Routing arrays: the plan's (routed already), or the pool's own.
-    const lora::RouteOut &rsrc = pre ? *pre : p->ro;
+    const lora::RouteOut &rsrc = pre ? *pre : cs.ro;
     a.rv = lora::RouteView{rsrc.perm, rsrc.pos_seg, rsrc.tok_pos, rsrc.tok_seg, rsrc.segs, rsrc.tiles, rsrc.n_tiles};
     a.tiles_bound = lora::max_tiles(n_tokens, p->S);
     a.policy = p->policy;
@@ -310,31 +378,35 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
         d.splits = dsplits;
         d.max_rank = p->R;
         d.theta = p->theta;
-        d.part = p->part;
+        d.part = cs.part;
         a.h_parts = dsplits;
         a.h_by_token = 1;
         HIP_TRY(mark(1));
         HIP_TRY(mark(2));
         // A routed call publishes into the pool's arrays (nobody reads them)
         // and leaves its statistics and error counter alone.
-        lora::RouteOut out = p->ro;
+        lora::RouteOut out = cs.ro;
         if (pre) out.stats = nullptr, out.err = nullptr;
         HIP_TRY(lora::launch_decode(a, d, token_adapter_idx, out, st, kev));
-        p->last_route_T = n_tokens;
-        p->last_route_stream = st;
+        if (!noalloc) {
+            p->last_route_T = n_tokens;
+            p->last_route_stream = st;
+        }
     } else {
         if (!pre) {
             HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
-                                       p->ro, st));
-            p->last_route_T = n_tokens;
-            p->last_route_stream = st;
+                                       cs.ro, st));
+            if (!noalloc) {
+                p->last_route_T = n_tokens;
+                p->last_route_stream = st;
+            }
         }
         HIP_TRY(mark(1));
         if (half) a.h_parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound);
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
         if (half) {
-            HIP_TRY(lora::launch_gemm_tiled(a, p->part, st, kev));
+            HIP_TRY(lora::launch_gemm_tiled(a, cs.part, st, kev));
         } else {
             HIP_TRY(lora::launch_base_gemm(a, st));
             HIP_TRY(mark(5));
@@ -344,7 +416,29 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
     HIP_TRY(mark(3));
     if (any_separate) HIP_TRY(half ? lora::launch_expand_sep16(a, st) : lora::launch_expand_separate(a, st));
     HIP_TRY(mark(4));
-    HIP_TRY(record_inflight(p, st));
+    if (noalloc) {
+        HIP_TRY(hipEventRecord(p->noalloc_done, st));
+        p->noalloc_used = true;
+    } else {
+        HIP_TRY(record_inflight(p, st));
+    }
+    return LORA_OK;
+}
+
+// The pool's own workspace.
+CallSpace pool_space(lora_pool p) { return CallSpace{p->ro, p->h, p->part}; }
+
+// Host-side checks shared by lora_apply and lora_apply_noalloc.
+int check_apply_args(lora_pool p, const void *x, const void *W_base, const int32_t *token_adapter_idx,
+                     int n_tokens, void *y) {
+    if (p == nullptr || n_tokens < 0) return LORA_EINVAL;
+    if (n_tokens == 0) return LORA_OK;
+    if (n_tokens > p->max_T) return LORA_ETOKENS;
+    if (x == nullptr || W_base == nullptr || token_adapter_idx == nullptr || y == nullptr) return LORA_EINVAL;
+    const size_t al = (p->esz == 2) ? 16 : 4;
+    if (!aligned(x, al) || !aligned(W_base, al) || !aligned(y, al) || !aligned(token_adapter_idx, 4))
+        return LORA_EINVAL;
+    if (x == y) return LORA_EINVAL;
     return LORA_OK;
 }
 
@@ -366,6 +460,7 @@ const char *lora_strerror(int status) {
         case LORA_EMISMATCH: return "shape or dtype does not match the pool";
         case LORA_ENOMEM: return "out of memory";
         case LORA_EHIP: return "HIP runtime error";
+        case LORA_ESCRATCH: return "call needs more workspace than the static scratch holds";
         default: return "unknown status";
     }
 }
@@ -414,6 +509,9 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
         return rc;
     };
     hipError_t e = hipGetDevice(&p->device);
+    // The device address of the static workspace (lora_apply_noalloc), once
+    // per device, with the device current.
+    if (e == hipSuccess) e = lora::scratch_setup(p->device);
     if (e != hipSuccess) return fail(hip_fail(e));
 
     const size_t S = static_cast<size_t>(n_slots);
@@ -476,6 +574,7 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     e = hipStreamCreateWithFlags(&p->internal, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->gate, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->data_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->noalloc_done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipMemsetAsync(p->A_slab, 0, a_bytes, p->internal);
     if (e == hipSuccess) e = hipMemsetAsync(p->B_slab, 0, b_bytes, p->internal);
     if (e == hipSuccess) e = hipMemsetAsync(p->slots_dev, 0, S * sizeof(lora::SlotDev), p->internal);
@@ -586,19 +685,31 @@ int lora_get_policy(lora_pool p, lora_mode *mode, int *threshold) {
 
 int lora_apply(lora_pool p, const void *x, const void *W_base, const int32_t *token_adapter_idx,
                int n_tokens, void *y, void *stream) {
-    if (p == nullptr || n_tokens < 0) return LORA_EINVAL;
-    if (n_tokens == 0) return LORA_OK;
-    if (n_tokens > p->max_T) return LORA_ETOKENS;
-    if (x == nullptr || W_base == nullptr || token_adapter_idx == nullptr || y == nullptr) return LORA_EINVAL;
-    const size_t al = (p->esz == 2) ? 16 : 4;
-    if (!aligned(x, al) || !aligned(W_base, al) || !aligned(y, al) || !aligned(token_adapter_idx, 4))
-        return LORA_EINVAL;
-    if (x == y) return LORA_EINVAL;
-
+    const int rc = check_apply_args(p, x, W_base, token_adapter_idx, n_tokens, y);
+    if (rc != LORA_OK || n_tokens == 0) return rc;
     std::lock_guard<std::mutex> lk(p->mu);
     DeviceGuard g(p->device);
     HIP_TRY(g.error());
-    return apply_locked(p, x, W_base, token_adapter_idx, n_tokens, y, static_cast<hipStream_t>(stream), nullptr);
+    return apply_locked(p, x, W_base, token_adapter_idx, n_tokens, y, static_cast<hipStream_t>(stream), nullptr,
+                        pool_space(p), false);
+}
+
+int lora_apply_noalloc(lora_pool p, const void *x, const void *W_base, const int32_t *token_adapter_idx,
+                       int n_tokens, void *y, void *stream) {
+    const int rc = check_apply_args(p, x, W_base, token_adapter_idx, n_tokens, y);
+    if (rc != LORA_OK || n_tokens == 0) return rc;
+    std::lock_guard<std::mutex> lk(p->mu);
+    // The static workspace's device address, resolved when the first pool
+    // was created on this device.
+    char *base = lora::scratch_device_ptr(p->device);
+    if (base == nullptr) return LORA_EHIP;
+    if (carve_call(p, n_tokens, nullptr, nullptr) > LORA_NOALLOC_SCRATCH_BYTES) return LORA_ESCRATCH;
+    CallSpace cs{};
+    carve_call(p, n_tokens, base, &cs);
+    DeviceGuard g(p->device);
+    HIP_TRY(g.error());
+    return apply_locked(p, x, W_base, token_adapter_idx, n_tokens, y, static_cast<hipStream_t>(stream), nullptr, cs,
+                        true);
 }
 
 int lora_route(lora_pool p, const int32_t *token_adapter_idx, int n_tokens, int32_t *counts, int32_t *offsets,
@@ -777,7 +888,8 @@ int lora_apply_routed(lora_pool p, lora_plan plan, const void *x, const void *W_
     }
     DeviceGuard g(p->device);
     HIP_TRY(g.error());
-    return apply_locked(p, x, W_base, plan->idx, n_tokens, y, static_cast<hipStream_t>(stream), &plan->ro);
+    return apply_locked(p, x, W_base, plan->idx, n_tokens, y, static_cast<hipStream_t>(stream), &plan->ro,
+                        pool_space(p), false);
 }
 
 int lora_loader_create(uint64_t capacity_bytes, lora_loader *out) {

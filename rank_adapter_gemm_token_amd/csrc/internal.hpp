@@ -161,6 +161,11 @@ int decode_token_blocks(int T);
 constexpr int MAX_TSPLIT = 8;
 int tiled_splits(int T, int d_in, int d_out);
 hipError_t launch_gemm_tiled(const ApplyArgs &a, float *part, hipStream_t st, LaunchEvents ev = {});
+// The static per-device workspace of lora_apply_noalloc (scratch.hip):
+// scratch_setup resolves its device address once per device (call with that
+// device current); scratch_device_ptr returns it (nullptr before set-up).
+hipError_t scratch_setup(int device);
+char *scratch_device_ptr(int device);
 // fp32 pools: VALU base GEMM and residual expand.
 hipError_t launch_base_gemm(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_expand_separate(const ApplyArgs &a, hipStream_t st);

@@ -35,13 +35,16 @@ LORA_EQUOTA = -7
 LORA_EMISMATCH = -8
 LORA_ENOMEM = -9
 LORA_EHIP = -10
+LORA_ESCRATCH = -11
+LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 DTYPE_OF = {torch.float32: LORA_F32, torch.float16: LORA_F16, torch.bfloat16: LORA_BF16}
 TORCH_DTYPE = {v: k for k, v in DTYPE_OF.items()}
 
 # Every symbol include/lora.h declares, in declaration order.
 EXPORTS = ["lora_pool_create", "lora_pool_destroy", "lora_set_tenant_quota", "lora_register",
-           "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_route", "lora_last_routing",
+           "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_apply_noalloc", "lora_route",
+           "lora_last_routing",
            "lora_plan_create", "lora_plan_destroy", "lora_plan_route", "lora_apply_routed",
            "lora_loader_create", "lora_loader_destroy", "lora_load_async", "lora_load_poll", "lora_load_wait",
            "lora_residency_create", "lora_residency_destroy", "lora_residency_set_share",
@@ -84,6 +87,7 @@ _lib.lora_unregister.argtypes = [_vp, _i]
 _lib.lora_set_policy.argtypes = [_vp, _i, _i]
 _lib.lora_get_policy.argtypes = [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i)]
 _lib.lora_apply.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
+_lib.lora_apply_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
 _lib.lora_route.argtypes = [_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.lora_last_routing.argtypes = [_vp, ctypes.POINTER(_i), _vp, _vp, _vp, _vp]
 _lib.lora_plan_create.argtypes = [_i, _i, ctypes.POINTER(_vp)]
@@ -222,6 +226,17 @@ def lora_apply(pool, x, W_base, token_adapter_idx, n_tokens, y, stream=None):
         _need(y, n_tokens * sh["d_out"], sh["dtype"], "y")
     _check(_lib.lora_apply(pool, _ptr(x), _ptr(W_base), _ptr(token_adapter_idx), int(n_tokens), _ptr(y),
                            _stream(stream)), "lora_apply")
+
+
+def lora_apply_noalloc(pool, x, W_base, token_adapter_idx, n_tokens, y, stream=None):
+    sh = _shapes.get(pool)
+    if sh is not None and 0 < n_tokens <= sh["max_T"]:
+        _need(x, n_tokens * sh["d_in"], sh["dtype"], "x")
+        _need(W_base, sh["d_out"] * sh["d_in"], sh["dtype"], "W_base")
+        _need(token_adapter_idx, n_tokens, torch.int32, "token_adapter_idx")
+        _need(y, n_tokens * sh["d_out"], sh["dtype"], "y")
+    _check(_lib.lora_apply_noalloc(pool, _ptr(x), _ptr(W_base), _ptr(token_adapter_idx), int(n_tokens), _ptr(y),
+                                   _stream(stream)), "lora_apply_noalloc")
 
 
 def lora_route(pool, token_adapter_idx, n_tokens, counts, offsets, perm, segs, n_seg, stream=None):
