@@ -132,21 +132,29 @@ def test_stats_struct_layout_matches_header(tmp_path):
     assert got[1:] == [getattr(L.lora_stats, f).offset for f in fields]
 
 
-def test_slot_book_and_ledger(tmp_path):
-    exe = tmp_path / "ledger_check"
-    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-o", str(exe),
-                    os.path.join(ROOT, "tests", "native", "ledger_check.cpp"),
-                    os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc", "ledger.cpp")],
-                   check=True)
-    r = subprocess.run([str(exe)], capture_output=True, text=True)
-    assert r.returncode == 0, r.stdout + r.stderr
+# The pure C++ parts of the host runtime (slot book and tenant ledger, LRU-K
+# residency policy), built plain and under AddressSanitizer + UBSan (host code
+# only; any report aborts the run).
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 
-def test_residency_policy(tmp_path):
-    exe = tmp_path / "residency_check"
-    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-o", str(exe),
-                    os.path.join(ROOT, "tests", "native", "residency_check.cpp"),
-                    os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc", "residency.cpp")],
+def _native_check(tmp_path, name, src, flags):
+    exe = tmp_path / name
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", *flags, "-o", str(exe),
+                    os.path.join(ROOT, "tests", "native", name + ".cpp"),
+                    os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc", src)],
                    check=True)
-    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env)
     assert r.returncode == 0, r.stdout + r.stderr
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr
+
+
+@pytest.mark.parametrize("flags", [[], SANITIZE], ids=["plain", "asan_ubsan"])
+def test_slot_book_and_ledger(tmp_path, flags):
+    _native_check(tmp_path, "ledger_check", "ledger.cpp", flags)
+
+
+@pytest.mark.parametrize("flags", [[], SANITIZE], ids=["plain", "asan_ubsan"])
+def test_residency_policy(tmp_path, flags):
+    _native_check(tmp_path, "residency_check", "residency.cpp", flags)
