@@ -209,3 +209,33 @@ def test_integer_inputs_exact(shape, dtype, limit, policy):
         assert np.array_equal(oracle.to_f64(y), ref)
     finally:
         p.close()
+
+
+# Decode calls keep partial sums and h in the pool's workspace between the
+# GEMM and its epilogue launch.
+DECODE_SHAPES = ["decode64", "decode5", "decodeS70"]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES)
+def test_decode_alternating_inputs(shape):
+    # Two different batches, one after the other many times on one stream: an
+    # epilogue that read another call's (stale) partial sums or h would break
+    # the equality with each batch's own first result.
+    x0, W, ads, idx0 = _normal_case(shape, "f16", 10)
+    x1, _, _, idx1 = _normal_case(shape, "f16", 11)
+    p = _pool(shape, "f16", lora.LORA_MODE_AUTO, ads, theta=0)
+    try:
+        Wd = dev(W)
+        ins = [(dev(x0), dev(idx0)), (dev(x1), dev(idx1))]
+        ref = [p.apply(x, Wd, i).cpu().view(torch.int16) for x, i in ins]
+        outs = []
+        for k in range(40):
+            x, i = ins[k % 2]
+            outs.append(p.apply(x, Wd, i))
+        torch.cuda.synchronize()
+        for k, y in enumerate(outs):
+            assert torch.equal(y.cpu().view(torch.int16), ref[k % 2]), k
+        r0, inv0 = reference(p, x0, W, idx0)
+        assert_close(outs[0].cpu(), r0, inv0, "f16")
+    finally:
+        p.close()

@@ -9,6 +9,7 @@ applies enqueued before the register and before those enqueued after it
 table), the outputs of one stream switch from NaN to correct once, never
 back."""
 import threading
+import time
 
 import numpy as np
 import pytest
@@ -70,16 +71,21 @@ def test_register_during_applies(seed):
         N = 300
         ys = [torch.empty((T, D), dtype=torch.float16, device="cuda") for _ in range(N)]
         torch.cuda.synchronize()
-        go = threading.Event()
+        go, started = threading.Event(), threading.Event()
 
         def applier():
             for i in range(N):
                 lora.lora_apply(p.h, xd, Wd, idd, T, ys[i], sa.cuda_stream)
                 if i == 40:
+                    # Let the register take the pool mutex while applies are
+                    # still in flight, and enqueue the rest after it.
                     go.set()
+                    started.wait()
+                    time.sleep(0.005)
 
         def registrar():
             go.wait()
+            started.set()
             lora.lora_register(p.h, 2, 2, A2, B2, R, 2.0 * R, sb.cuda_stream)
 
         th = [threading.Thread(target=applier), threading.Thread(target=registrar)]
