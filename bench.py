@@ -9,16 +9,25 @@ fused expand, separate expand.  Inputs are resident in HBM before timing.
 To keep the 256 MB last-level cache from serving the 32 MiB base weight,
 steps rotate over 16 independent (W, pool, x, idx, y) copies (>= 512 MiB).
 
+Other workloads: sweep<T> (100 adapters r8, Zipf), prefill, stack (the 7B
+linear stack), shard_col / shard_row (one GPU's 4096x512 / 512x4096 share of
+the decode q_proj under eight-way tensor parallelism).
+
 Prints ONE JSON line: tokens/s over K timed steps (HIP events on the stream
-the kernels run on, synchronize on both sides), the roofline of the dominant
-kernel (its algorithmic bytes over its average duration, timed with per-stage
-HIP events in a second pass of K steps), and the CPU fp64 oracle timed on the
-host cores on a bounded sample of the same workload.
+the kernels run on, synchronize on both sides), four more repeats of the same
+K steps and their median, the single-call latency of an isolated call, the
+roofline of the dominant kernel (its algorithmic bytes or FLOPs over its
+average duration, timed by the kernel's own dispatch events in a second pass
+of K steps), an achievable-peak calibration (a device copy, a device read and
+a large library matmul on the same GPU), and the CPU fp64 oracle timed on the
+host cores on a bounded sample of the same workload, plus single-thread oracle
+times of the tiny fp32 call and the decode call.
 """
 import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -39,9 +48,11 @@ CSRC = os.path.join(ROOT, "rank_adapter_gemm_token_amd", "csrc")
 KERNELS = {
     "decode": ("k_decode_gemm", ["gemm_decode.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
     "tiled": ("k_gemm_tiled", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
-    "split": ("k_gemm_lds<128, split>", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
+    "split": ("k_gemm_lds<64, split>", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
     "big": ("k_gemm_lds<256>", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
 }
+REPEATS = 5          # timed repeats of the K steps (the first is `value`)
+LATENCY_CALLS = 50   # isolated calls for the single-call latency
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -136,6 +147,14 @@ def setup(args, L):
         calls = build_linear_copies(L, w, w.linears[0], args.copies, args.policy, args.theta)
         steps = [[c] for c in calls]
         desc = "sweep 4096x4096 fp16, 100 adapters r8 alpha16, %d tokens, Zipf(1.1)" % T
+    elif args.workload in ("shard_col", "shard_row"):
+        kind = args.workload[len("shard_"):]
+        w = wl.shard(kind)
+        calls = build_linear_copies(L, w, w.linears[0], args.copies, args.policy, args.theta)
+        steps = [[c] for c in calls]
+        lin = w.linears[0]
+        desc = ("shard-%s: one GPU's share of the decode q_proj under 8-way tensor parallelism, "
+                "%dx%d fp16, 6 adapters r16 alpha32, 64 tokens (10%% base_only)" % (kind, lin.d_in, lin.d_out))
     elif args.workload == "prefill":
         w = wl.prefill()
         per = [build_linear_copies(L, w, lin, max(1, args.copies // 4), args.policy, args.theta)
@@ -201,7 +220,9 @@ def timed(L, steps, K):
     return t0.elapsed_time(t1) / 1e3
 
 
-def stage_profile(L, steps, K):
+def kernel_profile(L, steps, K):
+    """Device time of the dominant kernel per call, from the pair of events
+    its own dispatch records (lora_profile_enable), over K more steps."""
     pools = sorted({c.pool for s in steps for c in s})
     per_pool = {}
     for s in steps:
@@ -212,14 +233,13 @@ def stage_profile(L, steps, K):
     torch.cuda.synchronize()
     run_steps(L, steps, K)
     torch.cuda.synchronize()
-    tot = {"calls": 0, "route_ms": 0.0, "shrink_ms": 0.0, "gemm_ms": 0.0, "expand_ms": 0.0,
-           "kernel_ms": 0.0}
+    calls, kernel_ms = 0, 0.0
     for p in pools:
         r = L.lora_profile_read(p)
-        for k in tot:
-            tot[k] += r[k]
+        calls += r["calls"]
+        kernel_ms += r["kernel_ms"]
         L.lora_profile_enable(p, 0)
-    return tot
+    return kernel_ms / calls / 1e3
 
 
 def kernel_hash(kind):
@@ -260,6 +280,45 @@ def _oracle_rate(oracle, x, W, idx, S, ads, cores, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             return reps, el
+
+
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def single_thread_times():
+    """Single-thread oracle time per call of the tiny fp32 call (256x256, 16
+    tokens) and the decode call (4096x4096 fp16, 64 tokens), in seconds."""
+    import oracle
+    from rank_adapter_gemm_token_amd import workloads as wl
+    out = {}
+    for name, w, reps in (("tiny_256x256_f32_T16", wl.tiny(), 200), ("decode_4096x4096_f16_T64", wl.decode(), 1)):
+        lin = w.linears[0]
+        x = oracle.to_f64(w.x[lin.d_in])
+        W = oracle.to_f64(lin.W)
+        ads = {a.slot: (oracle.to_f64(a.A), oracle.to_f64(a.B), a.rank, a.alpha) for a in lin.adapters}
+        idx = w.idx.numpy()
+        oracle.apply(x[:1], W, idx[:1], w.S, ads, n_threads=1)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.apply(x, W, idx, w.S, ads, n_threads=1)
+        out[name] = (time.perf_counter() - t0) / reps
+    return out
 
 
 def cpu_baseline(w, seconds, workload):
@@ -314,10 +373,114 @@ def cpu_baseline(w, seconds, workload):
         value = w.T * reps / el
         what = "linear" if lin.name == "linear" else "%s linear" % lin.name
         sample = "%d full calls of the %s (%d tokens each, fp64, %.1f s)" % (reps, what, w.T, el)
-    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "sample": sample}
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "sample": sample,
+            "cpu_model": cpu_model(), "single_thread_s_per_call": single_thread_times()}
 
 
 # ----------------------------------------------------------------------------
+
+def device_info():
+    """The GPU's name, architecture, compute units and peak engine clock (from
+    rocminfo, run as a child process)."""
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory,
+            "max_clock_mhz": None}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        agent, arch = None, None
+        for line in out.splitlines():
+            t = line.strip()
+            if t.startswith("Name:") and "gfx" in t:
+                arch = t.split(":", 1)[1].strip()
+            if arch and t.startswith("Max Clock Freq. (MHz):"):
+                info["max_clock_mhz"] = int(t.split(":", 1)[1].strip())
+                break
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    return info
+
+
+def calibration(dtype):
+    """Achievable peaks on this GPU, from the probes in libcalibrate.so: one
+    pass of 16-byte non-temporal loads over a 1 GiB buffer (larger than the
+    256 MB last-level cache), a register-only loop of 16x16x32 MFMAs in the
+    workload's 16-bit type (fp16 for fp32 workloads), each the best of a few
+    grid sizes; plus a 1 GiB device-to-device torch copy (read + write bytes)."""
+    import ctypes
+    path = os.path.join(ROOT, "rank_adapter_gemm_token_amd", "libcalibrate.so")
+    if not os.path.exists(path):
+        log("calibration skipped: %s is not built" % path)
+        return None
+    lib = ctypes.CDLL(path)
+    lib.calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.calib_mfma_flops.restype = ctypes.c_double
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def per_launch(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError("calibration launch failed: %d" % rc)
+
+    n = 1 << 30
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    read = {}
+    for blocks in (1024, 2048, 4096):
+        t = per_launch(lambda: check(lib.calib_read(buf.data_ptr(), n, sink.data_ptr(), blocks, sp)), 10)
+        read[blocks] = n / t / 1e9
+    dst = torch.empty_like(buf)
+    t_copy = per_launch(lambda: dst.copy_(buf), 10)
+    del buf, dst
+    bf = 1 if dtype == "bf16" else 0
+    iters = 2000
+    mfma = {}
+    for blocks in (1024, 2048, 4096):
+        t = per_launch(lambda: check(lib.calib_mfma(bf, iters, sink.data_ptr(), blocks, sp)), 5)
+        mfma[blocks] = lib.calib_mfma_flops(iters, blocks) / t / 1e12
+    torch.cuda.empty_cache()
+    return {"read_GBs": max(read.values()), "read_GBs_by_blocks": read,
+            "mfma_TFLOPs": max(mfma.values()), "mfma_TFLOPs_by_blocks": mfma,
+            "copy_GBs": 2 * n / t_copy / 1e9,
+            "what": "libcalibrate.so: 1 GiB read once (16-byte non-temporal loads, grid-stride), "
+                    "register-only 16x16x32 %s MFMA loop (8 chains per wave); 1 GiB torch copy_ "
+                    "(read+write bytes); 10 (5) timed launches after one untimed" % ("bf16" if bf else "f16")}
+
+
+def single_call_latency(L, steps, n):
+    """Device time of one isolated step (GPU idle before it: synchronize,
+    event, the step's launches, event, synchronize), median over n."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    dev, host = [], []
+    for i in range(n):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        e0.record(stream)
+        run_steps(L, steps, 1, start=i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        host.append(time.perf_counter() - h0)
+        dev.append(e0.elapsed_time(e1) / 1e3)
+    dev.sort()
+    host.sort()
+    return {"device_us_median": 1e6 * dev[n // 2], "host_us_median": 1e6 * host[n // 2], "calls": n,
+            "what": "one step after a device synchronize: device time between events around its "
+                    "launches, and host time from before the launches to the end of the synchronize"}
+
 
 def loader_bench(L, args):
     """Adapter load latency through the async loader (lora_load_async): a
@@ -431,14 +594,15 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode",
-                    help="decode (default) | sweep<T> | prefill | stack")
+                    help="decode (default) | sweep<T> | prefill | stack | shard_col | shard_row")
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--policy", type=int, default=0, help="0 auto, 1 fused, 2 separate (with --theta)")
     ap.add_argument("--theta", type=int, default=None, help="threshold; default: the library's policy")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-profile", action="store_true", help="skip the per-stage pass")
+    ap.add_argument("--no-profile", action="store_true", help="skip the kernel-timing pass")
+    ap.add_argument("--no-calibration", action="store_true", help="skip the achievable-peak calibration")
     ap.add_argument("--route-per-call", action="store_true",
                     help="route every call (lora_apply) instead of once per step (lora_plan_route)")
     ap.add_argument("--loader", action="store_true",
@@ -479,6 +643,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     log("workload:", desc, "| step sets:", len(steps), "| calls/step:", len(steps[0]))
+    # Every rotating copy once (first touch), then the warm-up steps.
+    run_steps(L, steps, len(steps))
     run_steps(L, steps, args.warmup)
     torch.cuda.synchronize()
     sec = timed(L, steps, args.steps)
@@ -486,23 +652,21 @@ def main():
     value = tokens_per_step * args.steps / sec
     ms_per_step = sec * 1e3 / args.steps
     log("timed: %.3f ms/step, %.0f tokens/s" % (ms_per_step, value))
+    rep_ms = [ms_per_step] + [timed(L, steps, args.steps) * 1e3 / args.steps for _ in range(REPEATS - 1)]
+    log("repeats ms/step:", ["%.4f" % v for v in rep_ms])
+    latency = single_call_latency(L, steps, LATENCY_CALLS if len(steps[0]) == 1 else 3)
+    log("single-call latency:", latency)
 
     calls = steps[0]
     step_bytes = sum(c.call_bytes for c in calls)
     step_flops = sum(c.call_flops for c in calls)
     mfma_bound = args.workload == "prefill"
     roof = None
-    stages = None
     if not args.no_profile:
-        prof = stage_profile(L, steps, args.steps)
-        n = prof["calls"]
-        stages = {k: prof[k] / n for k in ("route_ms", "shrink_ms", "gemm_ms", "expand_ms")}
-        kernel_s = prof["kernel_ms"] / n / 1e3
-        log("per-call stage ms (events):", {k: round(v * 1e3, 2) for k, v in stages.items()}, "us")
         calls_per_step = len(calls)
         # The dominant kernel's own device time (dispatch timestamps recorded
         # by its launch), averaged over the K calls of the profile pass.
-        gemm_s = kernel_s
+        gemm_s = kernel_profile(L, steps, args.steps)
         if mfma_bound:
             achieved = (sum(c.gemm_flops for c in calls) / calls_per_step) / gemm_s / 1e12
             roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[w.dtype],
@@ -519,13 +683,21 @@ def main():
             kind = "decode"
         elif c0.T >= 2048 and c0.d_out % 256 == 0 and c0.d_in % 128 == 0:
             kind = "big"
-        elif c0.d_out % 128 == 0 and c0.d_in % 128 == 0:
+        elif c0.d_out % 64 == 0 and c0.d_in % 128 == 0:
             kind = "split"
         else:
             kind = "tiled"
         roof["kernel"] = KERNELS[kind][0]
         roof["kernel_us"] = gemm_s * 1e6
         roof["traffic"] = traffic_for(args.workload, kind)
+
+    calib = None
+    if not args.no_calibration:
+        calib = calibration(w.dtype)
+        log("calibration:", calib)
+        if roof is not None:
+            ach = calib["mfma_TFLOPs"] if roof["bound"] == "mfma" else calib["read_GBs"]
+            roof["frac_of_achievable"] = roof["achieved"] / ach
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -566,8 +738,11 @@ def main():
                           "mfma_TFLOPs": step_flops / step_s / 1e12,
                           "mfma_frac": step_flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]},
         "roofline": roof,
-        "stage_us_per_call": None if stages is None else {k.replace("_ms", ""): v * 1e3
-                                                          for k, v in stages.items()},
+        "repeats": {"ms_per_step": rep_ms, "median_ms_per_step": float(np.median(rep_ms)),
+                    "median_value": tokens_per_step / (float(np.median(rep_ms)) / 1e3)},
+        "single_call_latency": latency,
+        "calibration": calib,
+        "device": device_info(),
         "cpu_baseline": cpu,
         "zero_pad": zero_pad,
     }

@@ -430,8 +430,10 @@ typedef struct {
     double shrink_ms;
     double gemm_ms;     /* base projection with the fused expand.  fp16/bf16
                            calls of at most 64 tokens route and shrink inside
-                           the base-GEMM launch: route_ms and shrink_ms are 0
-                           and gemm_ms also holds its split-sum epilogue */
+                           their two launches and record no stage marks
+                           between them: route_ms, shrink_ms and expand_ms are
+                           0 and gemm_ms is the whole call (with the residual
+                           expand when a bucket runs SEPARATE) */
     double expand_ms;   /* separate residual expand */
     double kernel_ms;   /* device time of the base-GEMM kernel itself (fp16/
                            bf16 pools; 0 for fp32) */

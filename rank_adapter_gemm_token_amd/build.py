@@ -3,7 +3,9 @@
     python -m rank_adapter_gemm_token_amd.build [-v]
 
 Each source compiles to an object under _build/ in parallel, then hipcc links
-rank_adapter_gemm_token_amd/liblora.so.  Always recompiles.
+rank_adapter_gemm_token_amd/liblora.so.  Also links libcalibrate.so, the
+measurement harness's achievable-peak probes (no part of the library).
+Always recompiles.
 """
 import concurrent.futures as cf
 import os
@@ -15,11 +17,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblora.so")
+CALIB_LIB = os.path.join(PKG, "libcalibrate.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "ledger.cpp", "residency.cpp", "route.hip", "pad_copy.hip", "apply_kernels.hip", "gemm_decode.hip",
            "gemm_tiled.hip", "shrink_expand.hip", "scratch.hip"]
+CALIB_SOURCES = ["calibrate.hip"]
 
 # Packed-fp32 VALU instructions are kept out of every device object.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -45,16 +49,22 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], CALIB_LIB, verbose)
     return LIB
 
 

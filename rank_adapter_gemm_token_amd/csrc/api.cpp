@@ -87,7 +87,9 @@ struct lora_pool_s {
 
     lora::RouteOut ro{};
     float *h = nullptr;
-    float *part = nullptr;  // decode split-K partial sums
+    float *part = nullptr;  // split-K partial sums (decode and split tiles)
+    unsigned *split_cnt = nullptr;  // per-tile split counters of the split tiles (0 between calls)
+    int split_tiles = 0;            // counters at split_cnt
 
     hipStream_t internal = nullptr;
     std::mutex mu;
@@ -114,6 +116,7 @@ struct lora_pool_s {
     // Opt-in stage timing (lora_profile_enable).
     struct ProfSet {
         hipEvent_t e[7];  // stage marks 0..4; 5, 6: the base-GEMM kernel's own start / stop
+        bool staged;      // marks 1..3 recorded (paths with separate stage launches)
     };
     std::vector<ProfSet> prof;
     size_t prof_used = 0;
@@ -276,7 +279,7 @@ namespace {
 // DECODE_MAX_T tokens.
 int decode_splits_for(lora_pool p, int n_tokens) {
     if (p->esz != 2 || n_tokens < 1 || n_tokens > lora::DECODE_MAX_T) return 0;
-    return lora::decode_splits(n_tokens, p->d_in);
+    return lora::decode_splits(n_tokens, p->d_in, p->d_out);
 }
 
 // The device workspace one call's kernels use: the routing arrays (stats and
@@ -285,6 +288,7 @@ struct CallSpace {
     lora::RouteOut ro;
     float *h;
     float *part;
+    lora::SplitSpace split;  // partial sums and counters of the split tiles
 };
 
 // Lay out the workspace of one lora_apply_noalloc call of n_tokens (>= 1) on
@@ -316,8 +320,7 @@ size_t carve_call(lora_pool p, int n_tokens, char *base, CallSpace *cs) {
         part_floats = static_cast<size_t>(dsplits) * lora::decode_token_blocks(n_tokens) * 16 * p->d_out;
     } else if (p->esz == 2) {
         h_parts = static_cast<size_t>(lora::tiled_h_parts(p->d_in, p->Rp, lora::max_tiles(n_tokens, p->S)));
-        part_floats = static_cast<size_t>(lora::tiled_splits(n_tokens, p->d_in, p->d_out)) * ((T + 15) / 16 * 16) *
-                      p->d_out;
+        part_floats = lora::tiled_part_bytes(n_tokens, p->d_in, p->d_out) / 4;
     }
     const size_t o_h = take(h_parts * T * p->Rp * 4);
     const size_t o_part = take(part_floats * 4);
@@ -336,6 +339,9 @@ size_t carve_call(lora_pool p, int n_tokens, char *base, CallSpace *cs) {
         cs->ro.err = p->ro.err;
         cs->h = reinterpret_cast<float *>(base + o_h);
         cs->part = reinterpret_cast<float *>(base + o_part);
+        // The split counters sit in the scratch's own zeroed block (they are
+        // back at 0 after every call).
+        cs->split = lora::SplitSpace{cs->part, lora::scratch_split_counters(p->device), lora::MAX_SPLIT_TILES};
     }
     return off;
 }
@@ -347,6 +353,7 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
                  void *y, hipStream_t st, const lora::RouteOut *pre, const CallSpace &cs, bool noalloc) {
     lora_pool_s::ProfSet *ps = (p->prof_used < p->prof.size()) ? &p->prof[p->prof_used++] : nullptr;
     auto mark = [&](int i) { return ps ? hipEventRecord(ps->e[i], st) : hipSuccess; };
+    if (ps) ps->staged = false;
     lora::LaunchEvents kev{};
     if (ps) kev = lora::LaunchEvents{ps->e[5], ps->e[6]};
 
@@ -388,8 +395,6 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
         d.part = cs.part;
         a.h_parts = dsplits;
         a.h_by_token = 1;
-        HIP_TRY(mark(1));
-        HIP_TRY(mark(2));
         // A routed call publishes into the pool's arrays (nobody reads them)
         // and leaves its statistics and error counter alone.
         lora::RouteOut out = cs.ro;
@@ -400,6 +405,7 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
             p->last_route_stream = st;
         }
     } else {
+        if (ps) ps->staged = true;
         if (!pre) {
             HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
                                        cs.ro, st));
@@ -413,14 +419,14 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
         if (half) {
-            HIP_TRY(lora::launch_gemm_tiled(a, cs.part, st, kev));
+            HIP_TRY(lora::launch_gemm_tiled(a, cs.split, st, kev));
         } else {
             HIP_TRY(lora::launch_base_gemm(a, st));
             HIP_TRY(mark(5));
             HIP_TRY(mark(6));
         }
     }
-    HIP_TRY(mark(3));
+    if (ps && ps->staged) HIP_TRY(mark(3));
     if (any_separate) HIP_TRY(half ? lora::launch_expand_sep16(a, st) : lora::launch_expand_separate(a, st));
     HIP_TRY(mark(4));
     if (noalloc) {
@@ -433,7 +439,9 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
 }
 
 // The pool's own workspace.
-CallSpace pool_space(lora_pool p) { return CallSpace{p->ro, p->h, p->part}; }
+CallSpace pool_space(lora_pool p) {
+    return CallSpace{p->ro, p->h, p->part, lora::SplitSpace{p->part, p->split_cnt, p->split_tiles}};
+}
 
 // Host-side checks shared by lora_apply and lora_apply_noalloc.
 int check_apply_args(lora_pool p, const void *x, const void *W_base, const int32_t *token_adapter_idx,
@@ -549,7 +557,7 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     // h: fp32, [T][Rp]; calls of at most 64 tokens (fp16/bf16) keep one part
     // per k split of their GEMM, [splits][T][Rp], and the splits' partial
     // sums [splits][T rounded up to 16 .. 64][d_out].
-    const int dec_splits = (esz == 2) ? lora::decode_splits(static_cast<int>(dec_T), d_in) : 0;
+    const int dec_splits = (esz == 2) ? lora::decode_splits(static_cast<int>(dec_T), d_in, d_out) : 0;
     // Calls on the tiled path keep tiled_h_parts parts, [parts][T][Rp].
     size_t h_rows = std::max(T, static_cast<size_t>(dec_splits) * dec_T);
     if (esz == 2)
@@ -558,16 +566,17 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
                                           lora::tiled_h_parts(d_in, Rp, lora::max_tiles(t, n_slots)));
     const size_t o_h = take(h_rows * Rp * 4);
     const size_t dec_rows = static_cast<size_t>(lora::decode_token_blocks(static_cast<int>(dec_T))) * 16;
-    // Split-K partial sums of calls of 65 .. 2047 tokens: the largest
-    // splits x rows over the token counts the pool accepts.
+    // Split tiles of calls of 65 .. 2047 tokens: the largest partial-sum
+    // buffer and counter count over the token counts the pool accepts.
     size_t tiled_part = 0;
+    int split_tiles = 0;
     if (esz == 2)
-        for (int t = lora::DECODE_MAX_T + 1; t <= max_tokens && t < 2048; t += 16) {
-            const int tl = std::min(t + 15, std::min(max_tokens, 2047));
-            const size_t need = static_cast<size_t>(lora::tiled_splits(tl, d_in, d_out)) * ((tl + 15) / 16 * 16) * d_out;
-            tiled_part = std::max(tiled_part, need);
+        for (int t = lora::DECODE_MAX_T + 1; t <= max_tokens && t < 2048; ++t) {
+            tiled_part = std::max(tiled_part, lora::tiled_part_bytes(t, d_in, d_out));
+            split_tiles = std::max(split_tiles, lora::tiled_split_tiles(t, d_in, d_out));
         }
-    const size_t o_part = take(std::max(static_cast<size_t>(dec_splits) * dec_rows * d_out, tiled_part) * 4);
+    const size_t o_part = take(std::max(static_cast<size_t>(dec_splits) * dec_rows * d_out * 4, tiled_part));
+    const size_t o_cnt = take(static_cast<size_t>(split_tiles) * 4);
     const size_t ws_bytes = off;
 
     e = hipMalloc(&p->A_slab, a_bytes);
@@ -604,6 +613,8 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     p->ro.err = reinterpret_cast<unsigned long long *>(w + o_err);
     p->h = reinterpret_cast<float *>(w + o_h);
     p->part = reinterpret_cast<float *>(w + o_part);
+    p->split_cnt = reinterpret_cast<unsigned *>(w + o_cnt);  // zeroed with the workspace
+    p->split_tiles = split_tiles;
     *out = p;
     return LORA_OK;
 }
@@ -710,7 +721,8 @@ int lora_apply_noalloc(lora_pool p, const void *x, const void *W_base, const int
     // was created on this device.
     char *base = lora::scratch_device_ptr(p->device);
     if (base == nullptr) return LORA_EHIP;
-    if (carve_call(p, n_tokens, nullptr, nullptr) > LORA_NOALLOC_SCRATCH_BYTES) return LORA_ESCRATCH;
+    if (carve_call(p, n_tokens, nullptr, nullptr) > LORA_NOALLOC_SCRATCH_BYTES - lora::SCRATCH_COUNTER_BYTES)
+        return LORA_ESCRATCH;
     CallSpace cs{};
     carve_call(p, n_tokens, base, &cs);
     DeviceGuard g(p->device);
@@ -1252,10 +1264,18 @@ int lora_profile_read(lora_pool p, lora_profile *out) {
     for (size_t c = 0; c < p->prof_used; ++c) {
         lora_pool_s::ProfSet &ps = p->prof[c];
         HIP_TRY(hipEventSynchronize(ps.e[4]));
-        for (int i = 0; i < 4; ++i) {
+        if (ps.staged) {
+            for (int i = 0; i < 4; ++i) {
+                float ms = 0.0f;
+                HIP_TRY(hipEventElapsedTime(&ms, ps.e[i], ps.e[i + 1]));
+                *acc[i] += ms;
+            }
+        } else {
+            // One marked interval: the decode path's two launches and, when
+            // some bucket runs SEPARATE, the residual expand.
             float ms = 0.0f;
-            HIP_TRY(hipEventElapsedTime(&ms, ps.e[i], ps.e[i + 1]));
-            *acc[i] += ms;
+            HIP_TRY(hipEventElapsedTime(&ms, ps.e[0], ps.e[4]));
+            out->gemm_ms += ms;
         }
         float ms = 0.0f;
         HIP_TRY(hipEventElapsedTime(&ms, ps.e[5], ps.e[6]));

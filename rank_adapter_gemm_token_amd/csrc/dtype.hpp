@@ -82,6 +82,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              0x00020000);
 }
 
+// Cache-policy operand of the buffer memory intrinsics on gfx950: bit 4
+// (sc1) makes a load or store coherent at agent scope -- a store is written
+// through to the device's coherence point, a load does not use a copy that
+// another XCD's writes could have made stale.
+constexpr int CPOL_SC1 = 16;
+
 // 16-byte buffer load as an MFMA operand (byte offsets).
 template <typename V>
 __device__ __forceinline__ V bload8(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {

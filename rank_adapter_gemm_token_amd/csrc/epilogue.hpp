@@ -359,8 +359,7 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
                 if (js * 32 >= Rp) break;
                 V bf[NBB][WC];
 #pragma unroll
-                for (int b = 0; b < NBB; ++b)
-                    if (use[b] && js * 32 < rks[b]) load_b(keys[b], js, bf[b]);
+                for (int b = 0; b < NBB; ++b) load_b(use[b] && js * 32 < rks[b] ? keys[b] : 0, js, bf[b]);
 #pragma unroll
                 for (int b = 0; b < NBB; ++b) {
                     if (use[b] && js * 32 < rks[b]) {
@@ -373,7 +372,82 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
         }
         return;
     }
-    // Otherwise block by block, bucket by bucket.
+    if constexpr (TB * WC <= 8) {
+        // Several row blocks meeting several buckets: the wave's buckets (a
+        // run of bucket records, since rows are sorted) NBB at a time, each
+        // batch's B fragments requested together and multiplied into every
+        // block that holds rows of the batch's buckets.  A block's H operand
+        // (s * h of its rows of mode `want`) is formed once per rank step and
+        // masked to one bucket's rows per product; a bucket's slot, mode and
+        // rank come from the row facts of one of its rows (a ballot per
+        // block), so a batch costs one round of loads.  The B loads are
+        // unconditional (a bucket left out reads slot 0's B and is not
+        // multiplied): conditional loads make the compiler wait for every
+        // earlier load before each, one round per bucket.  The loops over
+        // rank steps and batches stay rolled (their code is fetched once).
+        constexpr int NBB = 8;
+        const int last_row = min(rows_end, p0 + TB * 16) - 1 - p0;  // >= 0: p0 < rows_end
+        const int g_lo = uniform(f.g[0]);
+        int g_hi = g_lo;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+            if (tb == last_row / 16) g_hi = __builtin_amdgcn_readlane(f.g[tb], last_row % 16);
+#pragma nounroll
+        for (int js = 0; js < JM; ++js) {
+            if (js * 32 >= Rp) break;
+            V hq[TB];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                float hv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (p0 + tb * 16 < rows_end) load_h(tb, js, hv);
+                hq[tb] = make_h(tb, js, -1, hv);
+            }
+#pragma nounroll
+            for (int gb = g_lo; gb <= g_hi; gb += NBB) {
+                int keys[NBB];
+                bool use[NBB];
+                uint32_t blocks[NBB];  // bit tb: block tb holds rows of the bucket
+#pragma unroll
+                for (int b = 0; b < NBB; ++b) {
+                    const int gg = gb + b;
+                    uint32_t bl = 0;
+                    int key = a.S, mode = SEG_NONE, rk = 0;
+#pragma unroll
+                    for (int tb = TB - 1; tb >= 0; --tb) {
+                        const unsigned long long m = __ballot(f.g[tb] == gg) & 0xFFFFull;
+                        if (m != 0) {
+                            const int l0 = __ffsll(static_cast<long long>(m)) - 1;
+                            bl |= 1u << tb;
+                            key = __builtin_amdgcn_readlane(f.key[tb], l0);
+                            mode = __builtin_amdgcn_readlane(f.mode[tb], l0);
+                            rk = __builtin_amdgcn_readlane(f.rank[tb], l0);
+                        }
+                    }
+                    use[b] = gg <= g_hi && bl != 0 && key < a.S && mode == want && js * 32 < rk;
+                    keys[b] = key;
+                    blocks[b] = bl;
+                }
+                V bf[NBB][WC];
+#pragma unroll
+                for (int b = 0; b < NBB; ++b) load_b(use[b] ? keys[b] : 0, js, bf[b]);
+#pragma unroll
+                for (int b = 0; b < NBB; ++b) {
+                    if (!use[b]) continue;
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        if ((blocks[b] >> tb) & 1u) {
+                            const V h = f.g[tb] == gb + b ? hq[tb] : zero8<V>();
+#pragma unroll
+                            for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(h, bf[b][wc], acc[tb][wc]);
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
+    // Wide wave tiles (registers for batches would not fit beside the
+    // accumulators): block by block, bucket by bucket.
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const int pb = p0 + tb * 16;

@@ -712,18 +712,25 @@ int decode_token_blocks(int T) {
     return tb;
 }
 
-int decode_splits(int T, int d_in) {
+int decode_splits(int T, int d_in, int d_out) {
     // Each GEMM wave takes at most DPAIRS_PER_WAVE step pairs (64 k each):
-    // at most NWK x DPAIRS_PER_WAVE pairs per split, at least 4 splits
-    // (64-column workgroups: d_out / 16 of them at d_out = 4096, one per CU);
-    // 0 beyond MAX_DSPLIT splits.  d_in is a multiple of 64.
+    // at least ceil(pairs / (NWK x DPAIRS_PER_WAVE)) splits, and at least 4.
+    // Narrow outputs (d_out / 64 column groups, fewer than 64 of them) take
+    // more splits, up to MAX_DSPLIT, so that the launch still spreads over
+    // the 256 CUs: a 512-wide shard runs 8 groups x 16 splits.  Every split
+    // keeps at least one pair; 0 beyond MAX_DSPLIT splits.  d_in and d_out
+    // are multiples of 64.
     (void)T;
     const int kp = d_in / 64;
     const int per = NWK * DPAIRS_PER_WAVE;
+    const int ncg = d_out / DCOLS;
     int s = (kp + per - 1) / per;
     if (s < 4) s = 4;
-    if (s > kp) s = kp;  // every split keeps at least one pair
-    return s <= MAX_DSPLIT ? s : 0;
+    if (s > MAX_DSPLIT) return 0;
+    const int fill = (256 + ncg - 1) / ncg;
+    if (s < fill) s = fill < MAX_DSPLIT ? fill : MAX_DSPLIT;
+    if (s > kp) s = kp;
+    return s;
 }
 
 hipError_t launch_decode(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx, const RouteOut &out,

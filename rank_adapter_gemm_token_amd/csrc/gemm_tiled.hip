@@ -3,8 +3,9 @@
 //   * k_gemm_lds<256> (>= 2048 tokens): 256 x 256 tiles staged into LDS by
 //     direct loads, the LoRA term computed into the accumulators before the
 //     main loop (described at its definition);
-//   * k_gemm_lds<128, split> + k_split_epilogue (65 .. 2047 tokens): the same
-//     staging over k ranges, fp32 partial sums, then sum + fused expand;
+//   * k_gemm_lds<64, split> (65 .. 2047 tokens): the same staging
+//     over k ranges; the splits of a tile add up inside the launch (the last
+//     one to finish sums them in split order) and apply the fused expand;
 //   * k_gemm_tiled (shapes off the 128 grid), described here.
 //
 // Here the projection is a dense contraction with enough rows to be bound by
@@ -134,9 +135,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
     store_rows<DT, TB, WC>(a, pw, a.T, nw, f, acc);
 }
 
-// 256-row tiles, operands straight into LDS.  A workgroup of 8 waves (2 x
-// 4) computes a 256 x BN output tile (BN = 256: each wave 128 rows x 64
-// columns; BN = 128: 128 x 32) over a range of k stages.  A 64-wide k stage
+// 256-row tiles, operands straight into LDS.  A workgroup of 8 waves computes
+// a 256 x BN output tile over a range of k stages: 2 x 4 waves of 128 rows x
+// BN/4 columns for BN = 256 and 128, 4 x 2 waves of 64 rows x 32 columns for
+// BN = 64 (fewer LDS operand reads per MFMA than 128 x 16).  A 64-wide k stage
 // is 16 row blocks of x and BN/16 of W, each 16 rows x 128 bytes (2 KiB) in
 // LDS.  Operands go from global memory into LDS directly (buffer_load_dwordx4
 // ... lds: lane l's 16 bytes land at instruction base + 16 l), one
@@ -157,9 +159,18 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
 // SPLIT = false (calls of >= 2048 tokens): all of d_in, then the fused
 // expand and the scatter to token order in the epilogue.
 // SPLIT = true (calls of 65 .. 2047 tokens, too few 256-row tiles to fill
-// the chip): workgroup z of the grid's third dimension takes the z-th of
-// gridDim.z k ranges and stores fp32 partial sums in MFMA fragment order;
-// k_split_epilogue adds them.
+// the chip): the grid is tiles x splits workgroups; split z of a tile takes
+// the z-th of `splits` k ranges.  With one split the workgroup finishes its
+// tile as the unsplit kernel does.  Otherwise each split stores its fp32
+// partial sums (MFMA fragment order, agent-coherent stores that reach the
+// memory side before the split is counted), then adds one to the tile's
+// counter; the split that brings it to `splits` resets it to 0 for the next
+// call, loads the other splits' partial sums (agent-coherent loads), adds
+// all of them in split order z = 0, 1, .. (so the sum does not depend on
+// which split finished last), adds the fused expand and stores y.  No
+// workgroup waits for another.  The splits of a tile are numbered so that the
+// hardware's round-robin dealing of workgroups to the 8 XCDs puts them on one
+// XCD when 8 divides the grid.
 using lds_ptr = __attribute__((address_space(3))) void *;
 
 // Byte offset of an LDS object.
@@ -204,38 +215,63 @@ __device__ __forceinline__ void xcd_tile_order(int nx, int ny, int id, int &tm, 
 }
 
 template <int DT, int BN, bool SPLIT>
-__global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
+__global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
     using E = Elem<DT>;
     using V = typename E::vec8;
-    constexpr int BM = 256, TB = 8, WC = BN / 64;
+    constexpr int BM = 256;
+    constexpr int WM = BN == 64 ? 4 : 2;  // waves along the rows
+    constexpr int WN = 8 / WM;            // waves along the columns
+    constexpr int TB = BM / 16 / WM;      // 16-row blocks per wave
+    constexpr int WC = BN / 16 / WN;      // 16-column blocks per wave
     constexpr int RBU = 128;             // 16-byte units per row block (16 rows x 128 B)
     constexpr int BOFF = 16 * RBU;       // W row blocks follow the 16 x row blocks
     constexpr int NBW = BN / 16;         // W row blocks per stage
     constexpr int BLD = NBW / 2;         // W load instructions per W wave (4 waves)
-    // Stage buffers: three at BN = 128 (two stages in flight while one is
-    // multiplied, 144 KiB), two at BN = 256 (128 KiB).
-    constexpr int NBUF = BN == 128 ? 3 : 2;
+    // Stage buffers: three at BN = 64 (two stages in flight while one is
+    // multiplied, 120 KiB), two at BN = 256 (128 KiB).
+    constexpr int NBUF = BN <= 128 ? 3 : 2;
     __shared__ u32x4_t lds0[(16 + NBW) * RBU];
     __shared__ u32x4_t lds1[(16 + NBW) * RBU];
     __shared__ u32x4_t lds2[NBUF == 3 ? (16 + NBW) * RBU : 1];
     // Output token of each sorted row of the tile (bitwise NOT of it for rows
     // of the invalid bucket), for the epilogue's stores.
     __shared__ int rowtok[SPLIT ? 1 : BM];
+    __shared__ int last_split;
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int g = lane >> 4;
-    const int wm = wave >> 2;  // rows wm * 128
-    const int wn = wave & 3;   // columns wn * BN / 4
-    int tm = blockIdx.y, tn = blockIdx.x;
-    if (!SPLIT) xcd_tile_order(gridDim.x, gridDim.y, blockIdx.x + gridDim.x * blockIdx.y, tm, tn);
+    const int wm = wave / WN;  // rows wm * TB * 16
+    const int wn = wave % WN;  // columns wn * WC * 16
+    int tm, tn, z = 0, tile = 0;
+    // Contributors per tile: the k splits, and the LoRA workgroup if the
+    // plan has one (contributor 0 of the tile, numbered z = splits).
+    const int nc = SPLIT ? sp.splits + sp.lora_wg : 1;
+    bool lora_role = false;
+    if constexpr (SPLIT) {
+        // Workgroup id -> (tile, contributor): ids are dealt to the XCDs
+        // round-robin (id mod 8), so when 8 divides the grid, XCD k takes the
+        // k-th eighth of the (tile, contributor) sequence, in which a tile's
+        // contributors follow one another.
+        const int n = sp.tiles * nc;
+        const int id = static_cast<int>(blockIdx.x);
+        const int q = uniform((n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id);
+        tile = uniform(q / nc);
+        const int j = uniform(q - tile * nc);
+        lora_role = sp.lora_wg && j == 0;
+        z = lora_role ? sp.splits : j - sp.lora_wg;
+        tm = tile / sp.tiles_x;
+        tn = tile - tm * sp.tiles_x;
+    } else {
+        xcd_tile_order(gridDim.x, gridDim.y, blockIdx.x + gridDim.x * blockIdx.y, tm, tn);
+    }
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     const int nst_all = a.d_in / 64;
-    const int s_beg = SPLIT ? uniform(static_cast<int>(blockIdx.z) * nst_all / static_cast<int>(gridDim.z)) : 0;
-    const int s_end = SPLIT ? uniform((static_cast<int>(blockIdx.z) + 1) * nst_all / static_cast<int>(gridDim.z))
-                            : nst_all;
+    // The LoRA workgroup multiplies no k stage.
+    const int s_beg = SPLIT ? (lora_role ? 0 : uniform(z * nst_all / sp.splits)) : 0;
+    const int s_end = SPLIT ? (lora_role ? 0 : uniform((z + 1) * nst_all / sp.splits)) : nst_all;
 
     // Loads: wave w < 4 fetches x row blocks 4w .. 4w+3 (8 instructions),
     // wave w >= 4 W row blocks (BLD instructions); instruction i covers row
@@ -250,7 +286,7 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     // MFMAs (rows past T are never stored).  Not in the unsplit kernel: the
     // branch around its MFMAs makes the compiler spill the accumulators.
     const int nld = xw ? ((SPLIT && m0 + (wave & 3) * 64 >= a.T) ? 0 : 8) : BLD;
-    const bool rows_live = !SPLIT || m0 + wm * TB * 16 < a.T;
+    const bool rows_live = !SPLIT || uniform(m0 + wm * TB * 16) < a.T;
     const __amdgpu_buffer_rsrc_t rs =
         xw ? make_rsrc(a.x, static_cast<uint32_t>(a.T) * a.d_in * 2)
            : make_rsrc(a.W, static_cast<uint32_t>(a.d_out) * a.d_in * 2);
@@ -347,8 +383,9 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
         } else if (xw) {
             asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         } else {
-            static_assert(BLD == 4 || BLD == 8, "W-wave load count");
-            if (BLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            static_assert(BLD == 2 || BLD == 4 || BLD == 8, "W-wave load count");
+            if (BLD == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+            else if (BLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
             else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         }
         // A bare barrier: __syncthreads() adds a workgroup fence, for which
@@ -377,7 +414,9 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
     };
 
     const int nst = s_end - s_beg;
-    if (NBUF == 2) {
+    if (nst == 0) {
+        // (The LoRA workgroup of a split tile.)
+    } else if (NBUF == 2) {
         issue(s_beg, lds0);
         if constexpr (!SPLIT) lora_prologue();
         for (int j = 0; j < nst; j += 2) {
@@ -418,63 +457,96 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, float *part) {
         static_assert(NBUF == 2, "the LoRA prologue runs in the two-buffer loop");
         store_rows_tok<DT, TB, WC>(a, pw, a.T, nw, rowtok + wm * TB * 16, acc);
     } else {
-        // Partial sums [z][16-row block][16-column block][lane], row blocks
-        // of sorted rows below T only; streaming stores (read once, by the
-        // split epilogue).
-        const int nrb = (a.T + 15) / 16, ncb = a.d_out / 16;
-        f32x4_t *pz = reinterpret_cast<f32x4_t *>(part) + static_cast<size_t>(blockIdx.z) * nrb * ncb * 64;
+        // The tile's sum: this workgroup's own with one contributor;
+        // otherwise the contributors' partial sums, added by the last one to
+        // finish: the k splits in split order z = 0, 1, .., then the LoRA
+        // workgroup's term if the plan has one (else the last contributor
+        // adds the fused expand itself).
+        f32x4_t sum[TB][WC];
+        RowFacts<TB> f;
+        if (lora_role && rows_live) {
+            // The LoRA workgroup: the tile's fused expand, s * h . B^T, from
+            // zero (its main loop took no k stage).
+            row_facts<TB>(a, pw, a.T, f);
+            lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, f, acc);
+        }
+        if (nc == 1) {
+            if (!rows_live) return;
+            row_facts_begin<TB>(a, pw, a.T, f);
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const int rb = pw / 16 + tb;
-            if (rb < nrb) {
+            for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-                for (int wc = 0; wc < WC; ++wc)
-                    __builtin_nontemporal_store(acc[tb][wc], &pz[(static_cast<size_t>(rb) * ncb + nw / 16 + wc) * 64 + lane]);
+                for (int wc = 0; wc < WC; ++wc) sum[tb][wc] = acc[tb][wc];
+        } else {
+            // This contributor's partial sums: wave w's TB x WC fragments at
+            // [z][tile][w][tb][wc][lane], the waves whose rows all lie past T
+            // left out (nobody reads them).
+            constexpr uint32_t FRB = TB * WC * 64 * 16;  // bytes per wave
+            const uint32_t zstride = static_cast<uint32_t>(sp.tiles) * 8 * FRB;
+            const __amdgpu_buffer_rsrc_t prs = make_rsrc(sp.part, static_cast<uint32_t>(nc) * zstride);
+            const uint32_t wbase = static_cast<uint32_t>(tile * 8 + wave) * FRB + lane * 16;
+            if (rows_live) {
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int wc = 0; wc < WC; ++wc)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[tb][wc]), prs,
+                                                               wbase + (tb * WC + wc) * 1024, z * zstride, CPOL_SC1);
+            }
+            // The stores are complete (at the agent's coherence point) before
+            // the contributor is counted.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const unsigned old =
+                    __hip_atomic_fetch_add(sp.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int last = old == static_cast<unsigned>(nc - 1);
+                if (last) __hip_atomic_store(sp.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last_split = last;
+            }
+            __syncthreads();
+            if (!last_split || !rows_live) return;
+            // The last contributor of the tile: the rows' routing facts and
+            // the other contributors' fragments requested together, NZ a
+            // round, then the sum in order (its own from registers).
+            if (!lora_role) row_facts_begin<TB>(a, pw, a.T, f);
+            constexpr int NZ = 2;
+#pragma unroll
+            for (int zb = 0; zb < MAX_TSPLIT + 1; zb += NZ) {
+                if (zb >= nc) break;
+                f32x4_t v[NZ][TB][WC];
+#pragma unroll
+                for (int jz = 0; jz < NZ; ++jz) {
+                    const int zz = zb + jz;
+                    if (zz < nc && zz != z) {
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                            for (int wc = 0; wc < WC; ++wc)
+                                v[jz][tb][wc] = __builtin_bit_cast(
+                                    f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 prs, wbase + (tb * WC + wc) * 1024, zz * zstride, CPOL_SC1));
+                    }
+                }
+#pragma unroll
+                for (int jz = 0; jz < NZ; ++jz) {
+                    const int zz = zb + jz;
+                    if (zz < nc) {
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                            for (int wc = 0; wc < WC; ++wc) {
+                                const f32x4_t u = zz == z ? acc[tb][wc] : v[jz][tb][wc];
+                                sum[tb][wc] = zz == 0 ? u : sum[tb][wc] + u;
+                            }
+                    }
+                }
             }
         }
+        if (!lora_role) row_facts_end<TB>(a, pw, a.T, f);
+        if (!sp.lora_wg) lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, f, sum);
+        store_rows<DT, TB, WC>(a, pw, a.T, nw, f, sum);
     }
-}
-
-// Split sums of k_gemm_lds<.., true>: workgroup of 4 waves over 64 sorted rows
-// x 16 WC columns, wave w = rows (4 blockIdx.y + w) * 16 .. +15.  Adds the
-// splits' partial sums in a fixed order, then the fused expand and the
-// scatter to token order, as the unsplit kernel's epilogue does.  WC = 2 for
-// calls of at most 256 tokens (twice the waves in flight for the same work),
-// else 4.
-template <int DT, int WC>
-__global__ __launch_bounds__(256) void k_split_epilogue(ApplyArgs a, const float *part, int splits) {
-    const int wave = uniform(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int rb = static_cast<int>(blockIdx.y) * 4 + wave;
-    const int nrb = (a.T + 15) / 16, ncb = a.d_out / 16;
-    if (rb >= nrb) return;
-    const int cb0 = static_cast<int>(blockIdx.x) * WC;
-    const f32x4_t *p = reinterpret_cast<const f32x4_t *>(part) + (static_cast<size_t>(rb) * ncb + cb0) * 64 + lane;
-    const size_t zs = static_cast<size_t>(nrb) * ncb * 64;
-    // Everything that does not depend on the routing facts is requested
-    // before them, behind their first round: the rows' buckets and tokens,
-    // then every split's partials (split index clamped, repeats not added, so
-    // the wait counts stay exact) and the rows' h.
-    RowFacts<1> f;
-    row_facts_begin<1>(a, rb * 16, a.T, f);
-    f32x4_t v[MAX_TSPLIT][WC];
-#pragma unroll
-    for (int z = 0; z < MAX_TSPLIT; ++z)
-#pragma unroll
-        for (int wc = 0; wc < WC; ++wc) v[z][wc] = p[min(z, splits - 1) * zs + wc * 64];
-    float hpre[2][8];
-    prefetch_h1(a, rb * 16, a.T, hpre);
-    row_facts_end<1>(a, rb * 16, a.T, f);
-    f32x4_t acc[1][WC];
-#pragma unroll
-    for (int wc = 0; wc < WC; ++wc) {
-        acc[0][wc] = v[0][wc];
-#pragma unroll
-        for (int z = 1; z < MAX_TSPLIT; ++z)
-            if (z < splits) acc[0][wc] += v[z][wc];
-    }
-    lora_expand_mfma<DT, 1, WC>(a, rb * 16, a.T, cb0 * 16, SEG_FUSED, f, acc, hpre);
-    store_rows<DT, 1, WC>(a, rb * 16, a.T, cb0 * 16, f, acc);
 }
 
 template <int DT, int BM, int BN>
@@ -485,25 +557,28 @@ hipError_t launch_shape(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
 }
 
 template <int DT>
-hipError_t launch_dt(const ApplyArgs &a, float *part, hipStream_t st, LaunchEvents ev) {
+hipError_t launch_dt(const ApplyArgs &a, const SplitSpace &ws, hipStream_t st, LaunchEvents ev) {
     if (a.T >= 2048 && a.d_out % 256 == 0 && a.d_in % 128 == 0) {
         const dim3 grid(a.d_out / 256, (a.T + 255) / 256);
-        LORA_LAUNCH(ev, (k_gemm_lds<DT, 256, false>), grid, dim3(512), 0, st, a, nullptr);
+        LORA_LAUNCH(ev, (k_gemm_lds<DT, 256, false>), grid, dim3(512), 0, st, a, SplitArgs{});
         return hipGetLastError();
     }
-    const int splits = tiled_splits(a.T, a.d_in, a.d_out);
-    if (splits > 0) {
-        const dim3 grid(a.d_out / 128, (a.T + 255) / 256, splits);
-        LORA_LAUNCH(ev, (k_gemm_lds<DT, 128, true>), grid, dim3(512), 0, st, a, part);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if (a.T <= 256) {
-            const dim3 egrid(a.d_out / 32, (a.T + 63) / 64);
-            hipLaunchKernelGGL((k_split_epilogue<DT, 2>), egrid, dim3(256), 0, st, a, part, splits);
-        } else {
-            const dim3 egrid(a.d_out / 64, (a.T + 63) / 64);
-            hipLaunchKernelGGL((k_split_epilogue<DT, 4>), egrid, dim3(256), 0, st, a, part, splits);
-        }
+    const TiledPlan tp = tiled_plan(a.T, a.d_in, a.d_out);
+    if (tp.splits > 0) {
+        SplitArgs sp{};
+        sp.splits = tp.splits;
+        sp.lora_wg = tp.lora_wg;
+        sp.tiles_x = a.d_out / tp.bn;
+        sp.tiles = sp.tiles_x * ((a.T + 255) / 256);
+        sp.part = ws.part;
+        sp.cnt = ws.cnt;
+        // The workspace was sized with tiled_part_bytes / tiled_split_tiles.
+        const int nc = tp.splits + tp.lora_wg;
+        if (nc > 1 && (ws.part == nullptr || ws.cnt == nullptr || sp.tiles > ws.max_tiles))
+            return hipErrorInvalidValue;
+        if (tp.bn != 64 || tp.splits > MAX_TSPLIT || tp.lora_wg > 1) return hipErrorInvalidValue;
+        const dim3 grid(sp.tiles * nc);
+        LORA_LAUNCH(ev, (k_gemm_lds<DT, 64, true>), grid, dim3(512), 0, st, a, sp);
         return hipGetLastError();
     }
     if (a.T >= 512 && a.d_out % 128 == 0) return launch_shape<DT, 128, 128>(a, st, ev);
@@ -512,20 +587,74 @@ hipError_t launch_dt(const ApplyArgs &a, float *part, hipStream_t st, LaunchEven
 
 }  // namespace
 
-int tiled_splits(int T, int d_in, int d_out) {
-    // Split-K for calls of 65 .. 2047 tokens: 256 x 128 tiles, the smallest
-    // power-of-two split (<= MAX_TSPLIT) that gives >= 256 workgroups with
-    // at least 4 k stages each; 0 when the shape does not fit the kernel
-    // (then the register-staged tiles run unsplit).
-    if (T <= DECODE_MAX_T || T >= 2048 || d_out % 128 != 0 || d_in % 128 != 0) return 0;
-    const int tiles = (d_out / 128) * ((T + 255) / 256);
-    int s = 1;
-    while (s < MAX_TSPLIT && tiles * s < 256 && d_in / 64 >= 8 * s) s *= 2;
-    return s;
+TiledPlan tiled_plan(int T, int d_in, int d_out) {
+    // Calls of 65 .. 2047 tokens with d_in a multiple of 128 and d_out of 64:
+    // 256 x 64 tiles, k split `splits` ways, plus (lora_wg = 1) a LoRA
+    // workgroup per tile that computes the fused expand beside the splits.
+    // The choice minimises a rough time model of one launch (per-CU rates
+    // measured on MI355X, rounded down): a workgroup streams its x rows and W
+    // rows through LDS at ~100 GB/s and multiplies at ~60% of a CU's MFMA
+    // peak; W streams from HBM at ~5 TB/s; with more than one contributor
+    // the fp32 partial sums make a round trip at ~5 TB/s and the last
+    // contributor reads the others' at ~100 GB/s; without a LoRA workgroup
+    // the last contributor's expand adds ~6 us (a few rounds of dependent
+    // loads).  A grid of more than 256 workgroups (one per CU) pays a round
+    // per 256; LoRA workgroups are taken only when the grid stays within one
+    // round.  (The same model prefers 64- over 128-column tiles at every T
+    // here: the wider tile needs more splits for the same grid.)  splits 0:
+    // not this path.
+    if (T <= DECODE_MAX_T || T >= 2048 || d_out % 64 != 0 || d_in % 128 != 0) return TiledPlan{0, 0, 0};
+    const int bn = 64;
+    const int row_tiles = (T + 255) / 256;
+    const double rows = T < 256 ? static_cast<double>((T + 63) / 64 * 64) : 256.0;  // x rows a tile loads
+    const int nst = d_in / 64;
+    const double w_s = static_cast<double>(d_in) * d_out * 2 / 5e12;
+    const double cu_mfma = 2.5e15 / 256 * 0.6;
+    const int tiles = d_out / bn * row_tiles;
+    TiledPlan best{0, 0, 0};
+    double best_t = 0.0;
+    for (int s = 1; s <= MAX_TSPLIT; ++s) {
+        if (s > 1 && nst / s < 4) break;
+        for (int lw = 0; lw <= 1; ++lw) {
+            const int nc = s + lw;
+            if (nc > 1 && (tiles > MAX_SPLIT_TILES ||
+                           static_cast<double>(nc) * tiles * 256 * bn * 4 >= 4294967296.0))
+                continue;
+            if (lw && tiles * nc > 256) continue;
+            const int rounds = (tiles * s + 255) / 256;
+            const int kst = (nst + s - 1) / s;
+            const double ingest = rounds * (rows + bn) * kst * 128 / 100e9;
+            const double mfma = rounds * rows * bn * kst * 64 * 2 / cu_mfma;
+            double t = std::max(std::max(ingest, mfma), w_s);
+            if (nc > 1) {
+                t += 2.0 * nc * tiles * rows * bn * 4 / 5e12;
+                t += (nc - 1) * rows * bn * 4 / 100e9;
+            }
+            if (!lw) t += 6e-6;
+            if (best.splits == 0 || t < best_t) {
+                best = TiledPlan{bn, s, lw};
+                best_t = t;
+            }
+        }
+    }
+    return best;
 }
 
-hipError_t launch_gemm_tiled(const ApplyArgs &a, float *part, hipStream_t st, LaunchEvents ev) {
-    return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, part, st, ev) : launch_dt<DT_BF16>(a, part, st, ev);
+size_t tiled_part_bytes(int T, int d_in, int d_out) {
+    const TiledPlan tp = tiled_plan(T, d_in, d_out);
+    const int nc = tp.splits + tp.lora_wg;
+    if (nc <= 1) return 0;
+    return static_cast<size_t>(nc) * (d_out / tp.bn) * ((T + 255) / 256) * 256 * tp.bn * 4;
+}
+
+int tiled_split_tiles(int T, int d_in, int d_out) {
+    const TiledPlan tp = tiled_plan(T, d_in, d_out);
+    if (tp.splits + tp.lora_wg <= 1) return 0;
+    return (d_out / tp.bn) * ((T + 255) / 256);
+}
+
+hipError_t launch_gemm_tiled(const ApplyArgs &a, const SplitSpace &ws, hipStream_t st, LaunchEvents ev) {
+    return (a.dtype == DT_F16) ? launch_dt<DT_F16>(a, ws, st, ev) : launch_dt<DT_BF16>(a, ws, st, ev);
 }
 
 }  // namespace lora

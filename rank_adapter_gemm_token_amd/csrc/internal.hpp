@@ -153,19 +153,49 @@ hipError_t launch_decode(const ApplyArgs &a, const DecodeArgs &d, const int32_t 
 hipError_t launch_route_small(const int32_t *idx, int T, int S, const SlotDev *slots, int max_rank, int policy,
                               int theta, const RouteOut &out, hipStream_t st);
 // k splits of the decode GEMM for (T, d_in); 0 if d_in is too large for it.
-int decode_splits(int T, int d_in);
+int decode_splits(int T, int d_in, int d_out);
 int decode_token_blocks(int T);
 // Larger calls (fp16/bf16): LDS-tiled MFMA GEMM with the fused expand.
-// Calls of 65 .. 2047 tokens may split k (tiled_splits > 0): `part` then
-// holds splits x ceil(T/16)*16 x d_out fp32 partial sums.
+// Calls of 65 .. 2047 tokens run 256-row tiles of `bn` columns with k split
+// `splits` ways, plus a LoRA workgroup per tile when lora_wg (tiled_plan;
+// splits 0: another kernel).  Tiles of more than one contributor keep their
+// fp32 partial sums in `part` (tiled_part_bytes) and one counter per tile in
+// `cnt` (tiled_split_tiles of them, 0 between calls: the last contributor of
+// a tile resets its counter).
 constexpr int MAX_TSPLIT = 8;
-int tiled_splits(int T, int d_in, int d_out);
-hipError_t launch_gemm_tiled(const ApplyArgs &a, float *part, hipStream_t st, LaunchEvents ev = {});
+constexpr int MAX_SPLIT_TILES = 16384;
+struct TiledPlan {
+    int bn;
+    int splits;
+    int lora_wg;         // 1: a LoRA workgroup per tile computes the fused expand
+};
+TiledPlan tiled_plan(int T, int d_in, int d_out);
+size_t tiled_part_bytes(int T, int d_in, int d_out);
+int tiled_split_tiles(int T, int d_in, int d_out);
+struct SplitSpace {
+    float *part = nullptr;
+    unsigned *cnt = nullptr;
+    int max_tiles = 0;   // counters available at cnt
+};
+struct SplitArgs {
+    int splits;
+    int lora_wg;
+    int tiles;           // output tiles (row tiles x tiles_x)
+    int tiles_x;         // column tiles
+    float *part;
+    unsigned *cnt;
+};
+hipError_t launch_gemm_tiled(const ApplyArgs &a, const SplitSpace &ws, hipStream_t st, LaunchEvents ev = {});
 // The static per-device workspace of lora_apply_noalloc (scratch.hip):
 // scratch_setup resolves its device address once per device (call with that
 // device current); scratch_device_ptr returns it (nullptr before set-up).
+// The array's first SCRATCH_COUNTER_BYTES hold the split tiles' counters
+// (zeroed at set-up, 0 between calls): scratch_split_counters; the per-call
+// workspace is carved from scratch_device_ptr, the rest.
+constexpr size_t SCRATCH_COUNTER_BYTES = static_cast<size_t>(MAX_SPLIT_TILES) * 4;
 hipError_t scratch_setup(int device);
 char *scratch_device_ptr(int device);
+unsigned *scratch_split_counters(int device);
 // fp32 pools: VALU base GEMM and residual expand.
 hipError_t launch_base_gemm(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_expand_separate(const ApplyArgs &a, hipStream_t st);

@@ -18,6 +18,10 @@ Workloads (all shapes are 7B-decoder shaped; "a x b" reads d_in x d_out):
   stack    32 layers x {q,k,v,o 4096x4096; gate,up 4096x11008; down 11008x4096}
            bf16, 64 adapters r=16 alpha=32 on every projection, 256 tokens,
            Zipf(1.1) idx + 5% base_only
+  shard    one GPU's share of the decode q_proj split eight ways: "col"
+           4096x512 (output columns sharded: W and B by column, A whole),
+           "row" 512x4096 (input rows sharded: W and A by row, B whole); 6
+           adapters r=16 alpha=32, 64 tokens, the decode idx
 
 Value distributions, N(0, v) with v the variance: x ~ N(0, 1); W, A ~
 N(0, 1/d_in); B ~ N(0, 0.01).  Small and medium tensors are drawn in fp64
@@ -132,6 +136,30 @@ def decode(seed=2, T=64) -> Workload:
     idx = draw_idx(rng, T, S, "uniform", base_only=0.10)
     return Workload("decode q_proj 4096x4096 fp16, 6 adapters r16, %d tokens" % T, "f16",
                     T, S, r, idx, {d: x}, [Linear("q_proj", d, d, W, ad)], seed)
+
+
+def shard(kind, seed=2, T=64, parts=8) -> Workload:
+    """The decode q_proj's per-GPU shard under eight-way tensor parallelism,
+    drawn with the decode workload's distributions (W, A ~ N(0, 1/4096), the
+    variance of the full 4096-wide projection)."""
+    rng = np.random.default_rng(seed + 100)
+    d, S, r = 4096, 6, 16
+    if kind == "col":
+        d_in, d_out = d, d // parts
+    elif kind == "row":
+        d_in, d_out = d // parts, d
+    else:
+        raise ValueError(kind)
+    x = normal(rng, (T, d_in), 1.0, "f16")
+    W = normal(rng, (d_out, d_in), 1.0 / d, "f16")
+    ad = []
+    for i in range(S):
+        ad.append(Adapter(slot=i, tenant=i, rank=r, alpha=32.0,
+                          A=normal(rng, (r, d_in), 1.0 / d, "f16"),
+                          B=normal(rng, (d_out, r), 0.01, "f16")))
+    idx = draw_idx(rng, T, S, "uniform", base_only=0.10)
+    return Workload("shard-%s q_proj %dx%d fp16, 6 adapters r16, %d tokens" % (kind, d_in, d_out, T), "f16",
+                    T, S, r, idx, {d_in: x}, [Linear("q_proj", d_in, d_out, W, ad)], seed)
 
 
 SWEEP_T = (1, 8, 16, 32, 64)

@@ -46,6 +46,15 @@ def test_sweep_fp16_full(T):
     _run_full(w, w.linears[0], lora.LORA_MODE_AUTO, 16)
 
 
+@pytest.mark.parametrize("kind", ["col", "row"])
+@pytest.mark.parametrize("policy,theta", POLICIES[:3])
+def test_shard_fp16_full(kind, policy, theta):
+    # One GPU's 4096x512 / 512x4096 share of the decode q_proj (the narrow
+    # one runs 16 k splits to spread over the CUs).
+    w = wl.shard(kind)
+    _run_full(w, w.linears[0], policy, theta)
+
+
 @pytest.mark.parametrize("proj", [0, 1])
 def test_prefill_bf16_sampled(proj):
     w = wl.prefill()
@@ -89,6 +98,13 @@ def _small_case(dtype, T, d_in, d_out, S, R, seed):
 # k part) and long and short buckets.
 # 96, 130 and 190 tokens take the split path with 64-row groups of the tile
 # wholly past T (their loads and MFMAs skipped).
+# Split tiles whose grid 8 does not divide (70 x 1024 -> 192: 3 tiles x 4
+# splits and a LoRA workgroup each; 100 x 2048 -> 960) put a tile's
+# contributors on different XCDs; 300 x 1024 -> 512 splits two rows of tiles;
+# 70 x 256 -> 64 is one split plus the LoRA workgroup, 300 x 256 -> 4096 one
+# split with the expand in the tile's own tail.
+# Narrow decode outputs take extra k splits (48 x 2048 -> 256: 16 splits of
+# 2 step pairs; 20 x 1024 -> 128: 16 splits of 1 pair).
 # Decode calls also cover pools beyond the epilogue's small-pool B tile (S R
 # > 1024) and beyond 64 slots (routing loads each token's slot entry; the GEMM
 # takes slots past its column groups in a second pass).
@@ -100,7 +116,10 @@ def _small_case(dtype, T, d_in, d_out, S, R, seed):
                                                (2200, 256, 256, 40, 16), (2300, 512, 256, 60, 64),
                                                (4100, 256, 256, 7, 64), (4096, 128, 128, 30, 24),
                                                (96, 256, 256, 9, 16), (130, 256, 384, 12, 32),
-                                               (190, 512, 256, 5, 64)])
+                                               (190, 512, 256, 5, 64), (48, 2048, 256, 6, 16),
+                                               (20, 1024, 128, 3, 32), (70, 1024, 192, 6, 16),
+                                               (100, 2048, 960, 9, 32), (300, 1024, 512, 13, 16),
+                                               (70, 256, 64, 5, 16), (300, 256, 4096, 7, 16)])
 @pytest.mark.parametrize("policy", [0, 1, 2])
 def test_small_ragged_full(dtype, T, d_in, d_out, S, R, policy):
     x, W, ads, idx = _small_case(dtype, T, d_in, d_out, S, R, seed=T * 31 + S)
@@ -112,6 +131,26 @@ def test_small_ragged_full(dtype, T, d_in, d_out, S, R, policy):
         y_ref, inv = reference(p, x, W, idx)
         assert_close(y.cpu(), y_ref, inv, dtype)
         assert p.poll_errors() == int(inv.sum())
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("policy", [0, 1, 2])
+def test_split_without_lora_workgroup_sampled(dtype, policy):
+    # 520 x 2048 -> 2048: 64 tiles (two rows of 256-row tiles) x 2 k splits
+    # and no LoRA workgroup (the grid would exceed one round of the CUs), so
+    # the last split of a tile adds the fused expand itself.
+    T, d_in, d_out, S, R = 520, 2048, 2048, 23, 32
+    x, W, ads, idx = _small_case(dtype, T, d_in, d_out, S, R, seed=520)
+    p = Pool(d_in, d_out, R, S, T, dtype, policy, 4)
+    try:
+        p.register_all(ads)
+        y = p.apply(dev(x), dev(W), dev(idx))
+        torch.cuda.synchronize()
+        rows = sample_rows(T, 96, seed=policy, must=[0, 255, 256, 511, 512, 519])
+        y_ref, inv = reference(p, x, W, idx, rows=rows)
+        assert_close(y.cpu()[torch.as_tensor(rows)], y_ref, inv, dtype)
     finally:
         p.close()
 

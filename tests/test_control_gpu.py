@@ -234,7 +234,9 @@ def test_stage_profile_counts_calls_and_stages():
             p.apply(dev(torch.randn(T, d).to(torch.float16)), W, dev(torch.zeros(T, dtype=torch.int32)))
         r = lora.lora_profile_read(p.h)
         assert r["calls"] == 3
-        assert r["gemm_ms"] > 0 and r["route_ms"] < r["gemm_ms"] and r["shrink_ms"] < r["gemm_ms"]
+        # Calls of at most 64 tokens: no separate route, shrink or expand
+        # launch, so those stages read exactly 0 and gemm_ms is the call.
+        assert r["gemm_ms"] > 0 and r["route_ms"] == 0 and r["shrink_ms"] == 0 and r["expand_ms"] == 0
         # The main kernel's own dispatch time lies inside its stage interval.
         assert 0 < r["kernel_ms"] <= r["gemm_ms"] + 1e-3
         assert min(r[k] for k in r if k.endswith("_ms")) >= 0

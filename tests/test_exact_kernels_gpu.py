@@ -6,10 +6,13 @@ depends on (T, d_in, d_out, dtype) only):
   decode64    k_decode_gemm, 4 token blocks, + k_decode_epilogue (T <= 64)
   decode5     the same with 1 token block
   decodeS70   the same, 70 slots over 4 column groups (second shrink pass)
-  split_wc2   k_gemm_lds<128, split> + k_split_epilogue, 32-column waves
-              (65 .. 256 tokens), 4 k splits, a 64-row x group past T
-  split_wc4   the same with 64-column waves (257 .. 2047 tokens), two
-              256-row tiles
+  decode_col  the same, 8 column groups x 16 k splits (narrow output)
+  split4      k_gemm_lds<64, split> (65 .. 2047 tokens), 4 tiles x 4 k
+              splits summed by the last split of each tile, a 64-row x
+              group past T
+  split2_rows2  the same, two 256-row tiles, 2 k splits
+  split_xcd   the same, 3 tiles x 4 splits (a grid 8 does not divide: a
+              tile's splits run on different XCDs)
   big         k_gemm_lds<256> (>= 2048 tokens, 256-row tiles)
   tiled       k_gemm_tiled (shapes off the 128 grid)
 
@@ -45,8 +48,10 @@ SHAPES = {
     "decode64": (64, 4096, 1024, 6, 16),
     "decode5": (5, 2048, 256, 4, 16),
     "decodeS70": (64, 512, 256, 70, 16),
-    "split_wc2": (130, 1024, 256, 9, 16),
-    "split_wc4": (300, 1024, 512, 9, 32),
+    "decode_col": (64, 4096, 512, 6, 16),   # 16 k splits over 8 column groups
+    "split4": (130, 1024, 256, 9, 16),      # 4 tiles x 4 splits
+    "split2_rows2": (300, 1024, 512, 9, 32),  # 16 tiles (2 rows) x 2 splits
+    "split_xcd": (70, 1024, 192, 6, 16),     # 3 tiles x 4 splits: splits on different XCDs
     "big": (2048, 256, 256, 12, 64),
     "tiled": (70, 128, 192, 6, 16),
 }

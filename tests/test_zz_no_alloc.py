@@ -85,9 +85,10 @@ def test_noalloc_against_oracle_separate_policy():
 
 
 def test_noalloc_refuses_calls_beyond_the_scratch():
-    # 256 tokens through an 11008-wide output take 4 k splits: 45 MB of fp32
-    # partial sums, beyond the 32 MiB array.  Refused before anything runs.
-    d_in, d_out, T = 4096, 11008, 256
+    # 512 tokens through an 8192 -> 11008 projection take 2 k splits of 344
+    # tiles: 43 MiB of fp32 partial sums, beyond the 32 MiB array.  Refused
+    # before anything runs.
+    d_in, d_out, T = 8192, 11008, 512
     p = Pool(d_in, d_out, 16, 2, T, "bf16")
     try:
         x = torch.zeros((T, d_in), dtype=torch.bfloat16, device="cuda")
