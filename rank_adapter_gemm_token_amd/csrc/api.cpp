@@ -319,7 +319,7 @@ size_t carve_call(lora_pool p, int n_tokens, char *base, CallSpace *cs) {
         h_parts = static_cast<size_t>(dsplits);
         part_floats = static_cast<size_t>(dsplits) * lora::decode_token_blocks(n_tokens) * 16 * p->d_out;
     } else if (p->esz == 2) {
-        h_parts = static_cast<size_t>(lora::tiled_h_parts(p->d_in, p->Rp, lora::max_tiles(n_tokens, p->S)));
+        h_parts = static_cast<size_t>(lora::tiled_h_parts(p->d_in, p->Rp, lora::max_tiles(n_tokens, p->S), n_tokens));
         part_floats = lora::tiled_part_bytes(n_tokens, p->d_in, p->d_out) / 4;
     }
     const size_t o_h = take(h_parts * T * p->Rp * 4);
@@ -372,6 +372,9 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
     a.slots = p->slots_dev;
     a.h = cs.h;
     a.h_parts = 1;
+    a.shrink_parts = 1;
+    a.shrink_g = 1;
+    a.cnt = cs.split.cnt;
     // Routing arrays: the plan's (routed already), or the pool's own.
     const lora::RouteOut &rsrc = pre ? *pre : cs.ro;
     a.rv = lora::RouteView{rsrc.perm, rsrc.pos_seg, rsrc.tok_pos, rsrc.tok_seg, rsrc.segs, rsrc.tiles, rsrc.n_tiles};
@@ -394,6 +397,7 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
         d.theta = p->theta;
         d.part = cs.part;
         a.h_parts = dsplits;
+        a.shrink_parts = dsplits;
         a.h_by_token = 1;
         // A routed call publishes into the pool's arrays (nobody reads them)
         // and leaves its statistics and error counter alone.
@@ -415,7 +419,15 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
             }
         }
         HIP_TRY(mark(1));
-        if (half) a.h_parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound);
+        if (half) {
+            // k parts of the shrink; the grouped shrink adds them into part 0
+            // itself (on the counters the split tiles also use, in stream
+            // order, each kernel leaving them at 0), so its consumers read one.
+            const int parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound, n_tokens);
+            a.shrink_g = lora::shrink_group(n_tokens, a.tiles_bound, cs.split.max_tiles);
+            a.shrink_parts = parts;
+            a.h_parts = a.shrink_g > 1 ? 1 : parts;
+        }
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
         if (half) {
@@ -563,18 +575,24 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     if (esz == 2)
         for (int t = 1; t <= max_tokens; ++t)
             h_rows = std::max(h_rows, static_cast<size_t>(t) *
-                                          lora::tiled_h_parts(d_in, Rp, lora::max_tiles(t, n_slots)));
+                                          lora::tiled_h_parts(d_in, Rp, lora::max_tiles(t, n_slots), t));
     const size_t o_h = take(h_rows * Rp * 4);
     const size_t dec_rows = static_cast<size_t>(lora::decode_token_blocks(static_cast<int>(dec_T))) * 16;
     // Split tiles of calls of 65 .. 2047 tokens: the largest partial-sum
     // buffer and counter count over the token counts the pool accepts.
     size_t tiled_part = 0;
     int split_tiles = 0;
-    if (esz == 2)
+    if (esz == 2) {
         for (int t = lora::DECODE_MAX_T + 1; t <= max_tokens && t < 2048; ++t) {
             tiled_part = std::max(tiled_part, lora::tiled_part_bytes(t, d_in, d_out));
             split_tiles = std::max(split_tiles, lora::tiled_split_tiles(t, d_in, d_out));
         }
+        // The grouped shrink's per-group counters share the array (calls of
+        // SHRINK_G_MIN_T tokens or more; the group count grows with T).
+        if (max_tokens >= lora::SHRINK_G_MIN_T)
+            split_tiles = std::max(split_tiles, (lora::max_tiles(max_tokens, n_slots) + lora::SHRINK_G - 1) /
+                                                    lora::SHRINK_G);
+    }
     const size_t o_part = take(std::max(static_cast<size_t>(dec_splits) * dec_rows * d_out * 4, tiled_part));
     const size_t o_cnt = take(static_cast<size_t>(split_tiles) * 4);
     const size_t ws_bytes = off;

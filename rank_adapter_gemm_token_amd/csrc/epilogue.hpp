@@ -38,7 +38,17 @@ __device__ __forceinline__ int token_of(const ApplyArgs &a, int p) {
 // waves and the waves' sums are added in LDS in a fixed order.  `lds` holds
 // >= NWV * RB * 64 16-byte words.  The part is written to h + part * T * R;
 // consumers add the parts in order.
-template <int DT, int RB, int NWV>
+// h element store: plain, or (SC1) coherent at agent scope, for parts that
+// another workgroup of the same launch adds up.
+template <bool SC1>
+__device__ __forceinline__ void store_h(float *p, float v) {
+    if constexpr (SC1)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
+template <int DT, int RB, int NWV, bool SC1 = false>
 __device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row0, int rows,
                                             const int32_t *perm, int part, u32x4_t *lds) {
     using E = Elem<DT>;
@@ -54,7 +64,7 @@ __device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row
     const int kq = lane >> 4;
     const int kst = a.d_in / 32;
     const int split = part * NWV + wave;  // this wave's share of K
-    const int nsplit = a.h_parts * NWV;
+    const int nsplit = a.shrink_parts * NWV;
     const int kb = split * kst / nsplit;
     const int ke = (split + 1) * kst / nsplit;
 
@@ -107,20 +117,20 @@ __device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = kq * 4 + i;
-            if (row < rows && j < Rp) hout[static_cast<size_t>(row0 + row) * Rp + j] = s[i];
+            if (row < rows && j < Rp) store_h<SC1>(&hout[static_cast<size_t>(row0 + row) * Rp + j], s[i]);
         }
     }
     for (int j = RB * 16 + r; j < Rp; j += 16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = kq * 4 + i;
-            if (row < rows) hout[static_cast<size_t>(row0 + row) * Rp + j] = 0.0f;
+            if (row < rows) store_h<SC1>(&hout[static_cast<size_t>(row0 + row) * Rp + j], 0.0f);
         }
     }
 }
 
 // shrink_unit for tile `tile` of the routing in global memory.
-template <int DT, int RB, int NWV>
+template <int DT, int RB, int NWV, bool SC1 = false>
 __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int part, u32x4_t *lds) {
     if (tile >= uniform(*a.rv.n_tiles)) return;
     const int tw = a.rv.tiles[2 * tile];
@@ -131,10 +141,10 @@ __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int pa
     const int rows = min(TILE_ROWS, end - row0);
     // Rank blocks that hold the slot's true rank (the tile carries it).
     const int nrb = uniform(min(RB, (tile_rank(tw) + 15) / 16));
-    if (RB >= 4 && nrb == 4) shrink_unit<DT, (RB >= 4 ? 4 : 1), NWV>(a, key, row0, rows, a.rv.perm, part, lds);
-    else if (RB >= 3 && nrb == 3) shrink_unit<DT, (RB >= 3 ? 3 : 1), NWV>(a, key, row0, rows, a.rv.perm, part, lds);
-    else if (RB >= 2 && nrb == 2) shrink_unit<DT, (RB >= 2 ? 2 : 1), NWV>(a, key, row0, rows, a.rv.perm, part, lds);
-    else shrink_unit<DT, 1, NWV>(a, key, row0, rows, a.rv.perm, part, lds);
+    if (RB >= 4 && nrb == 4) shrink_unit<DT, (RB >= 4 ? 4 : 1), NWV, SC1>(a, key, row0, rows, a.rv.perm, part, lds);
+    else if (RB >= 3 && nrb == 3) shrink_unit<DT, (RB >= 3 ? 3 : 1), NWV, SC1>(a, key, row0, rows, a.rv.perm, part, lds);
+    else if (RB >= 2 && nrb == 2) shrink_unit<DT, (RB >= 2 ? 2 : 1), NWV, SC1>(a, key, row0, rows, a.rv.perm, part, lds);
+    else shrink_unit<DT, 1, NWV, SC1>(a, key, row0, rows, a.rv.perm, part, lds);
 }
 
 // h[p][j .. j+7] summed over the shrink's k parts in order (p: the h row,

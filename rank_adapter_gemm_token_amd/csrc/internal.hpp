@@ -102,7 +102,11 @@ struct ApplyArgs {
     const void *B_slab; // [S][d_out][R]
     const SlotDev *slots;
     float *h;           // h_parts x [T][R] fp32; h = sum of the parts
-    int h_parts;        // k parts of the shrink, summed in order by the consumers
+    int h_parts;        // k parts of h the consumers read and add in order
+    int shrink_parts;   // k parts the shrink computes (= h_parts, or more when
+                        // the grouped shrink adds its parts into part 0 itself)
+    int shrink_g;       // bucket tiles per shrink workgroup (1 or SHRINK_G)
+    unsigned *cnt;      // per-group counters of the grouped shrink (0 between calls)
     int h_by_token;     // 1: h rows are indexed by token; 0: by sorted position
     RouteView rv;
     int tiles_bound;    // grid bound for tile-parallel kernels
@@ -114,7 +118,15 @@ hipError_t launch_shrink16(const ApplyArgs &a, hipStream_t st);
 // k parts of the fp16/bf16 shrink on the tiled path (h_parts) for a call of
 // at most `tiles` bucket tiles; consumers add the parts in order.
 constexpr int MAX_HPARTS = 8;
-int tiled_h_parts(int d_in, int R, int tiles);
+// Calls of at least SHRINK_G_MIN_T tokens group SHRINK_G bucket tiles per
+// shrink workgroup (shrink_group(T) = SHRINK_G, else 1).
+constexpr int SHRINK_G = 4;
+constexpr int SHRINK_G_MIN_T = 1024;
+// Calls of at least SHRINK_G_MIN_T tokens whose tile groups fit `counters`
+// use the grouped shrink: its k parts (tiled_h_parts) are added into part 0
+// by the shrink itself, and the consumers read one part.
+int shrink_group(int T, int tiles, int counters);
+int tiled_h_parts(int d_in, int R, int tiles, int T);
 hipError_t launch_expand_sep16(const ApplyArgs &a, hipStream_t st);
 // Optional timing events of one launch: when `start` is set, the kernel is
 // launched with hipExtLaunchKernelGGL, which records both events from the

@@ -77,8 +77,14 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
 
     // Keys.  Every index is read once (IDX_UNROLL per thread in flight); a
     // token's key is an LDS lookup of its slot's state, kept in LDS for the
-    // scatter when T <= KEY_CAP.
+    // scatter when T <= KEY_CAP.  The histogram adds one count per distinct
+    // key per wave: the lanes that share a key are found with one ballot per
+    // key bit and the lowest of them adds their number (one LDS atomic per
+    // key, instead of one per token: a wave of one adapter's tokens would
+    // otherwise serialise 64 atomics on one address).
     const bool keep = T <= KEY_CAP;
+    const int nbits = 32 - __clz(K);  // enough bits for keys 0..K (K = pad lanes)
+    const unsigned long long below = (1ull << lane) - 1ull;
     for (int t0 = 0; t0 < T; t0 += RT * IDX_UNROLL) {
         if (t0 > 0) {
 #pragma unroll
@@ -86,11 +92,20 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
         }
 #pragma unroll
         for (int u = 0; u < IDX_UNROLL; ++u) {
+            if (t0 + u * RT >= T) break;  // (uniform) no token in this round
             const int t = t0 + u * RT + tid;
-            if (t >= T) continue;
-            const int key = (vi[u] == -1) ? S : ((vi[u] >= 0 && vi[u] < S && s_act[vi[u]]) ? vi[u] : S + 1);
-            if (keep) s_key[t] = static_cast<unsigned short>(key);
-            atomicAdd(&s_cnt[key], 1);  // integer LDS atomics: counts do not depend on order
+            const bool v = t < T;
+            const int key = !v ? K
+                               : ((vi[u] == -1) ? S : ((vi[u] >= 0 && vi[u] < S && s_act[vi[u]]) ? vi[u] : S + 1));
+            if (v && keep) s_key[t] = static_cast<unsigned short>(key);
+            unsigned long long peers = ~0ull;
+            for (int b = 0; b < nbits; ++b) {
+                const int bit = (key >> b) & 1;
+                const unsigned long long m = __ballot(bit);
+                peers &= bit ? m : ~m;
+            }
+            // integer LDS atomics: counts do not depend on order
+            if (v && (peers & below) == 0) atomicAdd(&s_cnt[key], __popcll(peers));
         }
     }
     __syncthreads();
@@ -166,8 +181,6 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     }
 
     // Stable scatter, one chunk of RT tokens at a time.
-    const int nbits = 32 - __clz(K);  // enough bits for keys 0..K (K = pad lanes)
-    const unsigned long long below = (1ull << lane) - 1ull;
     for (int c0 = 0; c0 < T; c0 += RT) {
         const int t = c0 + tid;
         const bool v = t < T;
