@@ -52,6 +52,7 @@ KERNELS = {
     "big": ("k_gemm_lds<256>", ["gemm_tiled.hip", "epilogue.hpp", "dtype.hpp", "internal.hpp"]),
 }
 REPEATS = 5          # timed repeats of the K steps (the first is `value`)
+WARM_S = 0.2         # untimed warm-up before the W warm-up steps, seconds
 LATENCY_CALLS = 50   # isolated calls for the single-call latency
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -248,6 +249,66 @@ def kernel_hash(kind):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def workload_kind(workload):
+    """The dominant kernel's kind for a bench workload (the kernel the library
+    picks for its call shape, gemm_tiled.hip / gemm_decode.hip)."""
+    if workload in ("decode", "shard_col", "shard_row"):
+        return "decode"
+    if workload.startswith("sweep"):
+        return "decode" if int(workload[len("sweep"):] or 64) <= 64 else "split"
+    return {"prefill": "big", "stack": "split"}[workload]
+
+
+def write_counters(workload, fetch_dir, write_dir):
+    """profiles/counters.json entry for `workload` from two rocprofv3 --pmc
+    runs of its bench command (FETCH_SIZE, WRITE_SIZE; both with
+    --copy-calibration-mib 256): the dominant kernel's mean reading per
+    dispatch, each scaled by what the same counter reads for the run's 256 MiB
+    device copy, as HBM bytes per launch."""
+    import csv
+    import glob
+    kind = workload_kind(workload)
+    match = {"decode": "k_decode_gemm", "split": "k_gemm_lds<", "big": "k_gemm_lds<"}[kind]
+    must = {"decode": "", "split": ", true>", "big": ", false>"}[kind]
+
+    def read(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no counter_collection.csv under " + d)
+        vals, copy = [], []
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if "copyBuffer" in r["Kernel_Name"]:
+                    copy.append(v)
+                elif match in r["Kernel_Name"] and must in r["Kernel_Name"]:
+                    vals.append(v)
+        if not vals or not copy:
+            raise SystemExit("no %s readings for the kernel or the copy under %s" % (counter, d))
+        # the largest copy is the 256 MiB calibration copy
+        return sum(vals) / len(vals), len(vals), max(copy)
+
+    f_kib, n_f, f_copy = read(fetch_dir, "FETCH_SIZE")
+    w_kib, n_w, w_copy = read(write_dir, "WRITE_SIZE")
+    ff, wf = 262144.0 / f_copy, 262144.0 / w_copy
+    entry = {"kernel": KERNELS[kind][0], "kernel_sha": kernel_hash(kind),
+             "hbm_bytes_per_launch": (f_kib * ff + w_kib * wf) * 1024,
+             "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+             "fetch_factor": ff, "write_factor": wf, "dispatches": [n_f, n_w]}
+    try:
+        with open(COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = entry
+    with open(COUNTERS, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps({workload: entry}))
 
 
 def traffic_for(workload_key, kind):
@@ -610,11 +671,17 @@ def main():
     ap.add_argument("--loader-rounds", type=int, default=20)
     ap.add_argument("--theta-sweep", action="store_true",
                     help="run the fused/separate threshold sweep instead of the bench step")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the workload's profiles/counters.json entry from two rocprofv3 --pmc "
+                         "output directories (FETCH_SIZE, WRITE_SIZE) of its bench command; no GPU")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warm-up, run two plain device-to-device copies of this many MiB "
                          "(the known-size reference for hardware byte counters)")
     args = ap.parse_args()
 
+    if args.write_counters:
+        write_counters(args.workload, *args.write_counters)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -643,8 +710,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     log("workload:", desc, "| step sets:", len(steps), "| calls/step:", len(steps[0]))
-    # Every rotating copy once (first touch), then the warm-up steps.
+    # Every rotating copy once (first touch), untimed steps for at least
+    # WARM_S seconds (clocks settle: with a few short steps the first timed
+    # pass of a sub-millisecond step ran ~10% slow), then the warm-up steps.
     run_steps(L, steps, len(steps))
+    t_warm, i_warm = time.perf_counter(), 0
+    while True:
+        run_steps(L, steps, len(steps), start=i_warm)
+        i_warm += len(steps)
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_warm >= WARM_S:
+            break
     run_steps(L, steps, args.warmup)
     torch.cuda.synchronize()
     sec = timed(L, steps, args.steps)
@@ -676,17 +752,7 @@ def main():
             achieved = per_launch / gemm_s / 1e9
             roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS}
-        c0 = calls[0]
-        # The kernel the library picks for this call shape (gemm_tiled.hip,
-        # gemm_decode.hip).
-        if c0.T <= 64:
-            kind = "decode"
-        elif c0.T >= 2048 and c0.d_out % 256 == 0 and c0.d_in % 128 == 0:
-            kind = "big"
-        elif c0.d_out % 64 == 0 and c0.d_in % 128 == 0:
-            kind = "split"
-        else:
-            kind = "tiled"
+        kind = workload_kind(args.workload)
         roof["kernel"] = KERNELS[kind][0]
         roof["kernel_us"] = gemm_s * 1e6
         roof["traffic"] = traffic_for(args.workload, kind)
