@@ -194,33 +194,48 @@ __global__ __launch_bounds__(256) void k_shrink_grouped(ApplyArgs a) {
     if (!last) return;
     // The group's rows: each tile's 16 rows (fewer at the end of a bucket),
     // Rp floats each, contiguous in every part (rows are h rows by sorted
-    // position); 4 floats a lane, every part's loads of a tile together.
+    // position): at most 16 Rp / 4 <= 256 float4 a tile, one per thread.
+    // Every tile's and every part's loads are issued before the first add
+    // (clamped offsets keep them unconditional); a run of one bucket's tiles
+    // needs no tile records (16 rows apart from row0).
     const int Rp = a.R;
     const uint32_t pstride = static_cast<uint32_t>(a.T) * Rp * 4;
     const __amdgpu_buffer_rsrc_t hrs = make_rsrc(a.h, static_cast<uint32_t>(P) * pstride);
+    uint32_t off[G];
+    bool ok[G];
 #pragma unroll
     for (int ti = 0; ti < G; ++ti) {
         const int t = t0 + ti;
-        if (t >= n_tiles) break;
-        const int tw = uniform(a.rv.tiles[2 * t]);
-        const int sg = tile_seg(tw);
-        const int r0 = uniform(a.rv.tiles[2 * t + 1]);
-        const int e = uniform(a.rv.segs[4 * sg + 1] + a.rv.segs[4 * sg + 2]);
-        const int n4 = min(16, e - r0) * Rp / 4;  // float4 of the tile (Rp is a multiple of 8)
-        for (int q = threadIdx.x; q < n4; q += 256) {
-            const uint32_t off = static_cast<uint32_t>(r0) * Rp * 4 + q * 16;
-            f32x4_t v[MAXP];
-#pragma unroll
-            for (int pp = 0; pp < MAXP; ++pp)
-                if (pp < P)
-                    v[pp] = __builtin_bit_cast(f32x4_t,
-                                               __builtin_amdgcn_raw_buffer_load_b128(hrs, off, pp * pstride, CPOL_SC1));
-            f32x4_t sm = v[0];
-#pragma unroll
-            for (int pp = 1; pp < MAXP; ++pp)
-                if (pp < P) sm += v[pp];
-            *reinterpret_cast<f32x4_t *>(reinterpret_cast<char *>(a.h) + off) = sm;
+        int r0, e;
+        if (one) {
+            r0 = row0 + ti * 16;
+            e = end;
+        } else {
+            const int tc = min(t, n_tiles - 1);
+            r0 = a.rv.tiles[2 * tc + 1];
+            const int sg = tile_seg(a.rv.tiles[2 * tc]);
+            e = a.rv.segs[4 * sg + 1] + a.rv.segs[4 * sg + 2];
         }
+        const int n4 = min(16, e - r0) * Rp / 4;  // float4 of the tile (Rp is a multiple of 8)
+        ok[ti] = t < n_tiles && static_cast<int>(threadIdx.x) < n4;
+        off[ti] = ok[ti] ? static_cast<uint32_t>(r0) * Rp * 4 + threadIdx.x * 16 : 0u;
+    }
+    f32x4_t v[G][MAXP];
+#pragma unroll
+    for (int ti = 0; ti < G; ++ti)
+#pragma unroll
+        for (int pp = 0; pp < MAXP; ++pp)
+            if (pp < P)
+                v[ti][pp] = __builtin_bit_cast(
+                    f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hrs, off[ti], pp * pstride, CPOL_SC1));
+#pragma unroll
+    for (int ti = 0; ti < G; ++ti) {
+        if (!ok[ti]) continue;
+        f32x4_t sm = v[ti][0];
+#pragma unroll
+        for (int pp = 1; pp < MAXP; ++pp)
+            if (pp < P) sm += v[ti][pp];
+        *reinterpret_cast<f32x4_t *>(reinterpret_cast<char *>(a.h) + off[ti]) = sm;
     }
 }
 
