@@ -314,7 +314,7 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int RS = Ring::SLOTS;
     constexpr int L = Ring::LOADS;
     static_assert(RS >= 1 && RS <= 4, "ring");
-    static_assert(NWK * NB * 64 <= NWK * RS * Ring::UNITS, "cross-wave sums fit in the ring");
+    static_assert(NWK * (NB + TB * RB) * 64 <= NWK * RS * Ring::UNITS, "cross-wave sums fit in the ring");
     // Per-wave rings of step pairs; after the main loop, the cross-wave sums.
     __shared__ u32x4_t smem[NWK * RS * Ring::UNITS];
 
@@ -380,9 +380,14 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int i = 0; i < RS; ++i)
         issue_pair(xrs, wrs, ring + (i % RS) * Ring::UNITS, loff, Ring::XROWS / 8, L, pair_off(i));
-    // Adapter index of token `lane` (every wave holds all T of them), used
-    // by the shrink at the end.
+    // Adapter index of token `lane` (every wave holds all T of them), and
+    // the state of slot cg, used by the shrink at the end (a vector load:
+    // its wait is at the end, behind the ring's).
     const int my_idx = idx[min(lane, T - 1)];
+    const int state0 = shrink0 ? __builtin_amdgcn_raw_buffer_load_b32(
+                                     make_rsrc(a.slots, static_cast<uint32_t>(a.S) * sizeof(SlotDev)),
+                                     static_cast<uint32_t>(cg) * sizeof(SlotDev), 0, 0)
+                               : SLOT_FREE;
 
     // 3. Base GEMM (and the shrink of slot cg) pair by pair.  Operand reads:
     //    lane (r, kq) of half h takes row r of a block, chunk 4 h + kq, at
@@ -438,13 +443,21 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     // 4. The 4 waves' sums in LDS (the ring is free once every wave is past
     //    its last pair), added in a fixed order (wave 0 + 1 + 2 + 3), stored
     //    as this split's partial sums, fragment order [q][16-column
-    //    block][tb][lane] (16 bytes a lane).
+    //    block][tb][lane] (16 bytes a lane).  The shrink's sums (slot cg)
+    //    take the same LDS round, after the GEMM's.
     f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
+    f32x4_t *hred = red + NWK * NB * 64;
     __syncthreads();
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int c = 0; c < DCB; ++c) red[((wave * TB + tb) * DCB + c) * 64 + lane] = acc[tb][c];
+    if (shrink0) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int jb = 0; jb < RB; ++jb) hred[((wave * TB + tb) * RB + jb) * 64 + lane] = hacc[tb][jb];
+    }
     __syncthreads();
     f32x4_t *part = reinterpret_cast<f32x4_t *>(d.part);
 #pragma unroll
@@ -462,17 +475,13 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     //    the tokens of slot s (fp32, by token, part q); the 4 waves' sums
     //    added in order.
     float *hout = a.h + static_cast<size_t>(q) * T * Rp;
-    auto store_h = [&](unsigned long long mask, const f32x4_t (&hc)[TB][RB]) {
-        __syncthreads();  // red free
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int jb = 0; jb < RB; ++jb) red[((wave * TB + tb) * RB + jb) * 64 + lane] = hc[tb][jb];
-        __syncthreads();
+    // Adds the 4 waves' h fragments at `hr` in order and stores the rows of
+    // `mask`'s tokens.
+    auto sum_store_h = [&](unsigned long long mask, const f32x4_t *hr) {
         for (int f = wave; f < TB * RB; f += NWK) {
-            f32x4_t v = red[f * 64 + lane];
+            f32x4_t v = hr[f * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < NWK; ++w) v += red[(w * TB * RB + f) * 64 + lane];
+            for (int w = 1; w < NWK; ++w) v += hr[(w * TB * RB + f) * 64 + lane];
             const int tb = f / RB, j = (f % RB) * 16 + r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -481,9 +490,18 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
     };
+    auto store_h = [&](unsigned long long mask, const f32x4_t (&hc)[TB][RB]) {
+        __syncthreads();  // red free
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int jb = 0; jb < RB; ++jb) red[((wave * TB + tb) * RB + jb) * 64 + lane] = hc[tb][jb];
+        __syncthreads();
+        sum_store_h(mask, red);
+    };
     if (shrink0) {
         const unsigned long long mask = __ballot(lane < T && my_idx == cg);
-        if (mask != 0 && uniform(a.slots[cg].state) == SLOT_ACTIVE) store_h(mask, hacc);
+        if (mask != 0 && uniform(state0) == SLOT_ACTIVE) sum_store_h(mask, hred);
     }
     // Slots cg + ncg, cg + 2 ncg, ... (pools of more slots than column
     // groups): x fragments read again, straight from global memory.
@@ -546,35 +564,35 @@ __global__ __launch_bounds__((NWK + 1) * 64) void k_decode_epilogue(ApplyArgs a,
     const int nb = blockIdx.x;  // 16-column block
     const int n = nb * 16 + (lane & 15);
 
+    // Every LoRA bucket runs fused under the FUSED policy and under AUTO with
+    // a threshold below 1 (a bucket holds at least one token).  Then a row's
+    // treatment follows from its own slot entry, and the row waves do not
+    // wait for the routing, which only workgroup 0 computes (to publish it).
+    const bool all_fused = a.policy == 1 || (a.policy == 0 && d.theta < 1);
     if (wave == NWK) {
         // Routing wave: token index, then its slot entry; the routing in LDS,
-        // published by workgroup 0.
+        // published by workgroup 0.  With all buckets fused it meets the row
+        // waves' barrier first and routes afterwards.
+        if (all_fused) {
+            __syncthreads();
+            if (blockIdx.x != 0) return;
+        }
         const int v = lane < T ? idx[min(lane, T - 1)] : -1;
         const int2 e = reinterpret_cast<const int2 *>(a.slots)[2 * min(max(v, 0), a.S - 1)];
         small_route(v, e.x, e.y, T, a.S, d.max_rank, a.policy, d.theta, sr);
         if (blockIdx.x == 0) publish_route(sr, T, out);
-        __syncthreads();
+        if (!all_fused) __syncthreads();
         return;
     }
 
-    // Row waves: the adapter index of this thread's 4 rows, then, as soon as
-    // they arrive, the B rows and scales of their slots (clamped: used only
-    // for FUSED rows, whose key is that index); then the splits' partial sums
-    // and the h parts.
+    // Row waves: the adapter index of this thread's 4 rows; the first group
+    // of splits' partial sums and h parts (which do not depend on it); then,
+    // as soon as the indices arrive, the B rows and slot entries of their
+    // slots (clamped: used only for FUSED rows, whose key is that index).
     const int tb = min(wave, TB - 1);
     int vi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) vi[i] = idx[min(tb * 16 + (lane >> 4) * 4 + i, T - 1)];
-    u32x4_t bw[4][2 * RB];
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int kc = min(max(vi[i], 0), a.S - 1);
-        const uint16_t *bp = static_cast<const uint16_t *>(a.B_slab) + (static_cast<size_t>(kc) * a.d_out + n) * Rp;
-#pragma unroll
-        for (int qb = 0; qb < 2 * RB; ++qb) bw[i][qb] = *reinterpret_cast<const u32x4_t *>(bp + min(8 * qb, Rp - 8));
-        sc[i] = a.slots[kc].scale;
-    }
     // Splits are taken SQ at a time (4: all of them at once for d_in <=
     // 4096; 2 at ranks above 32, for registers), each group's loads in
     // flight together, and added in split order.
@@ -584,13 +602,11 @@ __global__ __launch_bounds__((NWK + 1) * 64) void k_decode_epilogue(ApplyArgs a,
     const int hq_n = T * Rp / 4;
     const size_t pstride = static_cast<size_t>(T) * Rp / 4;
     const float4 *hp = reinterpret_cast<const float4 *>(a.h);
-    f32x4_t acc;
-    float4 hsum[HQ];
-    for (int q0 = 0; q0 < d.splits; q0 += SQ) {
-        f32x4_t pv[SQ];
-        float4 hv[HQ][SQ];
-        // Unconditional loads (split index clamped; the repeats are not
-        // added), so the wait counts stay exact.
+    f32x4_t pv[SQ];
+    float4 hv[HQ][SQ];
+    // Unconditional loads (split index clamped; the repeats are not added),
+    // so the wait counts stay exact.
+    auto load_group = [&](int q0) {
 #pragma unroll
         for (int u = 0; u < SQ; ++u) pv[u] = part[min(q0 + u, d.splits - 1) * qstride];
 #pragma unroll
@@ -598,6 +614,24 @@ __global__ __launch_bounds__((NWK + 1) * 64) void k_decode_epilogue(ApplyArgs a,
 #pragma unroll
             for (int u = 0; u < SQ; ++u)
                 hv[m][u] = hp[min(q0 + u, d.splits - 1) * pstride + min(tid + m * NWK * 64, hq_n - 1)];
+    };
+    load_group(0);
+    u32x4_t bw[4][2 * RB];
+    float sc[4];
+    int st[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int kc = min(max(vi[i], 0), a.S - 1);
+        const uint16_t *bp = static_cast<const uint16_t *>(a.B_slab) + (static_cast<size_t>(kc) * a.d_out + n) * Rp;
+#pragma unroll
+        for (int qb = 0; qb < 2 * RB; ++qb) bw[i][qb] = *reinterpret_cast<const u32x4_t *>(bp + min(8 * qb, Rp - 8));
+        sc[i] = a.slots[kc].scale;
+        st[i] = a.slots[kc].state;
+    }
+    f32x4_t acc;
+    float4 hsum[HQ];
+    for (int q0 = 0; q0 < d.splits; q0 += SQ) {
+        if (q0 > 0) load_group(q0);
         asm volatile("" ::: "memory");  // every load of the group is issued before the first add
         if (q0 == 0) {
             acc = pv[0];
@@ -634,15 +668,23 @@ __global__ __launch_bounds__((NWK + 1) * 64) void k_decode_epilogue(ApplyArgs a,
     if (wave >= TB) return;
 
     // FUSED rows: the key of a LoRA token is its adapter index, so the B
-    // rows loaded above are its slot's.
+    // rows loaded above are its slot's.  With every bucket fused the key
+    // follows from the token's own index and slot entry (as the routing
+    // defines it); otherwise from the routing's bucket records.
     int key[4];
     bool fused[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = tb * 16 + (lane >> 4) * 4 + i;
-        const int sg = sr.tok_seg[min(t, T - 1)];
-        key[i] = sr.segs[sg][0];
-        fused[i] = t < T && key[i] < a.S && sr.segs[sg][3] == SEG_FUSED;
+        if (all_fused) {
+            const int v = vi[i];
+            key[i] = v == -1 ? a.S : (v >= 0 && v < a.S && st[i] == SLOT_ACTIVE) ? v : a.S + 1;
+            fused[i] = t < T && key[i] < a.S;
+        } else {
+            const int sg = sr.tok_seg[min(t, T - 1)];
+            key[i] = sr.segs[sg][0];
+            fused[i] = t < T && key[i] < a.S && sr.segs[sg][3] == SEG_FUSED;
+        }
     }
     raw *y = static_cast<raw *>(a.y);
 #pragma unroll
