@@ -303,6 +303,30 @@ struct DecRing {
     static constexpr int SLOTS = FIT < DPAIRS_PER_WAVE ? FIT : DPAIRS_PER_WAVE;
 };
 
+// The A fragments of `slot` for a wave's k step pairs (pair i of the wave is
+// split pair wave + NWK i, clamped to the split's pn pairs from pa): lane
+// (r, kq) holds rank row jb * 16 + r (clamped), k 8 kq .. 8 kq + 7 of each
+// 32-wide step.
+template <typename V, int PPW, int RB>
+__device__ __forceinline__ void load_a_frags(const ApplyArgs &a, int slot, int pa, int pn, int wave,
+                                             V (&f)[PPW][2][RB]) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;
+    const int kq = lane >> 4;
+    const int Rp = a.R;
+    const uint32_t rowb = static_cast<uint32_t>(a.d_in) * 2;
+    const __amdgpu_buffer_rsrc_t ars =
+        make_rsrc(static_cast<const uint16_t *>(a.A_slab) + static_cast<size_t>(slot) * Rp * a.d_in, Rp * rowb);
+#pragma unroll
+    for (int i = 0; i < PPW; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int jb = 0; jb < RB; ++jb)
+                f[i][h][jb] = bload8<V>(ars, static_cast<uint32_t>(min(jb * 16 + r, Rp - 1)) * rowb + 16 * kq,
+                                        static_cast<uint32_t>(2 * (pa + min(wave + NWK * i, pn - 1)) + h) * 64);
+}
+
 template <int DT, int TB, int RB>
 __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_decode_gemm(
     ApplyArgs a, DecodeArgs d, const int32_t *__restrict__ idx) {
@@ -314,7 +338,8 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int RS = Ring::SLOTS;
     constexpr int L = Ring::LOADS;
     static_assert(RS >= 1 && RS <= 4, "ring");
-    static_assert(NWK * (NB + TB * RB) * 64 <= NWK * RS * Ring::UNITS, "cross-wave sums fit in the ring");
+    static_assert(NWK * (NB + (RB <= 2 ? 2 : 1) * TB * RB) * 64 <= NWK * RS * Ring::UNITS,
+                  "cross-wave sums fit in the ring");
     // Per-wave rings of step pairs; after the main loop, the cross-wave sums.
     __shared__ u32x4_t smem[NWK * RS * Ring::UNITS];
 
@@ -340,20 +365,23 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     // 1. The A fragments of slot cg for this wave's steps (requested before
     //    the token indices are known: a slot is named by few tokens if any).
-    V af[PPW][2][RB];
+    //    Pools of more slots than column groups take slot cg + ncg in the
+    //    main loop as well (HS = 2, ranks up to 32: the sums' LDS round has
+    //    room for both); slots past those are added after it.
+    constexpr int HS = RB <= 2 ? 2 : 1;
+    V af[HS][PPW][2][RB];
     const bool shrink0 = cg < a.S;
-    if (shrink0) {
-        const __amdgpu_buffer_rsrc_t ars =
-            make_rsrc(static_cast<const uint16_t *>(a.A_slab) + static_cast<size_t>(cg) * Rp * a.d_in, Rp * rowb);
-#pragma unroll
-        for (int i = 0; i < PPW; ++i)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int jb = 0; jb < RB; ++jb)
-                    af[i][h][jb] = bload8<V>(ars, static_cast<uint32_t>(min(jb * 16 + r, Rp - 1)) * rowb + 16 * kq,
-                                             static_cast<uint32_t>(2 * (pa + min(pair_of(i), pn - 1)) + h) * 64);
-    }
+    const bool shrink1 = HS == 2 && cg + ncg < a.S;
+    if (shrink0) load_a_frags<V, PPW, RB>(a, cg, pa, pn, wave, af[0]);
+    if (shrink1) load_a_frags<V, PPW, RB>(a, cg + ncg, pa, pn, wave, af[HS - 1]);
+    // The states of those slots, used by the shrink's stores at the end
+    // (vector loads, older than the ring's: no wait count changes).
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.slots, static_cast<uint32_t>(a.S) * sizeof(SlotDev));
+    const int state0 = shrink0 ? __builtin_amdgcn_raw_buffer_load_b32(srs, static_cast<uint32_t>(cg) * sizeof(SlotDev), 0, 0)
+                               : SLOT_FREE;
+    const int state1 =
+        shrink1 ? __builtin_amdgcn_raw_buffer_load_b32(srs, static_cast<uint32_t>(cg + ncg) * sizeof(SlotDev), 0, 0)
+                : SLOT_FREE;
 
     // 2. Step pairs straight into this wave's ring slots: one instruction per
     //    8 rows, 8 lanes a row covering its 128-byte line; the chunk a lane
@@ -380,14 +408,9 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int i = 0; i < RS; ++i)
         issue_pair(xrs, wrs, ring + (i % RS) * Ring::UNITS, loff, Ring::XROWS / 8, L, pair_off(i));
-    // Adapter index of token `lane` (every wave holds all T of them), and
-    // the state of slot cg, used by the shrink at the end (a vector load:
-    // its wait is at the end, behind the ring's).
+    // Adapter index of token `lane` (every wave holds all T of them), used
+    // by the shrink at the end.
     const int my_idx = idx[min(lane, T - 1)];
-    const int state0 = shrink0 ? __builtin_amdgcn_raw_buffer_load_b32(
-                                     make_rsrc(a.slots, static_cast<uint32_t>(a.S) * sizeof(SlotDev)),
-                                     static_cast<uint32_t>(cg) * sizeof(SlotDev), 0, 0)
-                               : SLOT_FREE;
 
     // 3. Base GEMM (and the shrink of slot cg) pair by pair.  Operand reads:
     //    lane (r, kq) of half h takes row r of a block, chunk 4 h + kq, at
@@ -395,13 +418,15 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int sw = r & 7;
     const int lo[2] = {r * 8 + ((0 + kq) ^ sw), r * 8 + ((4 + kq) ^ sw)};
     f32x4_t acc[TB][DCB];
-    f32x4_t hacc[TB][RB];
+    f32x4_t hacc[HS][TB][RB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
         for (int c = 0; c < DCB; ++c) acc[tb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jb = 0; jb < RB; ++jb) hacc[tb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int hs = 0; hs < HS; ++hs)
+#pragma unroll
+            for (int jb = 0; jb < RB; ++jb) hacc[hs][tb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
@@ -428,12 +453,16 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
                 for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
                     for (int c = 0; c < DCB; ++c) acc[tb][c] = E::mfma(xf[h][tb], wf[h][c], acc[tb][c]);
-                if (shrink0) {
 #pragma unroll
-                    for (int jb = 0; jb < RB; ++jb) {
-                        const V am = (jb * 16 + r < Rp) ? af[i][h][jb] : zero8<V>();
+                for (int hs = 0; hs < HS; ++hs) {
+                    if (hs == 0 ? shrink0 : shrink1) {
 #pragma unroll
-                        for (int tb = 0; tb < TB; ++tb) hacc[tb][jb] = E::mfma(xf[h][tb], am, hacc[tb][jb]);
+                        for (int jb = 0; jb < RB; ++jb) {
+                            const V am = (jb * 16 + r < Rp) ? af[hs][i][h][jb] : zero8<V>();
+#pragma unroll
+                            for (int tb = 0; tb < TB; ++tb)
+                                hacc[hs][tb][jb] = E::mfma(xf[h][tb], am, hacc[hs][tb][jb]);
+                        }
                     }
                 }
             }
@@ -443,20 +472,24 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     // 4. The 4 waves' sums in LDS (the ring is free once every wave is past
     //    its last pair), added in a fixed order (wave 0 + 1 + 2 + 3), stored
     //    as this split's partial sums, fragment order [q][16-column
-    //    block][tb][lane] (16 bytes a lane).  The shrink's sums (slot cg)
-    //    take the same LDS round, after the GEMM's.
+    //    block][tb][lane] (16 bytes a lane).  The shrink's sums (slots cg
+    //    and cg + ncg) take the same LDS round, after the GEMM's.
     f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
-    f32x4_t *hred = red + NWK * NB * 64;
+    f32x4_t *hred = red + NWK * NB * 64;  // slot hs at hred + hs * NWK * TB * RB * 64
     __syncthreads();
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int c = 0; c < DCB; ++c) red[((wave * TB + tb) * DCB + c) * 64 + lane] = acc[tb][c];
-    if (shrink0) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
+    for (int hs = 0; hs < HS; ++hs) {
+        if (hs == 0 ? shrink0 : shrink1) {
 #pragma unroll
-            for (int jb = 0; jb < RB; ++jb) hred[((wave * TB + tb) * RB + jb) * 64 + lane] = hacc[tb][jb];
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int jb = 0; jb < RB; ++jb)
+                    hred[((hs * NWK + wave) * TB + tb) * RB * 64 + jb * 64 + lane] = hacc[hs][tb][jb];
+        }
     }
     __syncthreads();
     f32x4_t *part = reinterpret_cast<f32x4_t *>(d.part);
@@ -503,9 +536,13 @@ __global__ __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
         const unsigned long long mask = __ballot(lane < T && my_idx == cg);
         if (mask != 0 && uniform(state0) == SLOT_ACTIVE) sum_store_h(mask, hred);
     }
-    // Slots cg + ncg, cg + 2 ncg, ... (pools of more slots than column
-    // groups): x fragments read again, straight from global memory.
-    for (int s = cg + ncg; s < a.S; s += ncg) {
+    if (shrink1) {
+        const unsigned long long mask = __ballot(lane < T && my_idx == cg + ncg);
+        if (mask != 0 && uniform(state1) == SLOT_ACTIVE) sum_store_h(mask, hred + NWK * TB * RB * 64);
+    }
+    // Slots cg + HS ncg, ... (pools of more slots than HS column groups):
+    // x fragments read again, straight from global memory.
+    for (int s = cg + HS * ncg; s < a.S; s += ncg) {
         const unsigned long long mask = __ballot(lane < T && my_idx == s);
         if (mask == 0) continue;
         if (uniform(a.slots[s].state) != SLOT_ACTIVE) continue;
