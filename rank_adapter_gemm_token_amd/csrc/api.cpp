@@ -207,16 +207,28 @@ void free_pool_memory(lora_pool p) {
 // call on MI355X (one record per lora_apply).
 constexpr unsigned kCompletionEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 
-// Record completion of the work just enqueued on `st`.
-hipError_t record_inflight(lora_pool p, hipStream_t st) {
+// The completion event of the pool's work on `st` (created on first use, not
+// recorded here).
+hipError_t inflight_event(lora_pool p, hipStream_t st, hipEvent_t *out) {
     for (auto &se : p->inflight) {
-        if (se.first == st) return hipEventRecord(se.second, st);
+        if (se.first == st) {
+            *out = se.second;
+            return hipSuccess;
+        }
     }
     hipEvent_t ev = nullptr;
     hipError_t e = hipEventCreateWithFlags(&ev, kCompletionEventFlags);
     if (e != hipSuccess) return e;
     p->inflight.emplace_back(st, ev);
-    return hipEventRecord(ev, st);
+    *out = ev;
+    return hipSuccess;
+}
+
+// Record completion of the work just enqueued on `st`.
+hipError_t record_inflight(lora_pool p, hipStream_t st) {
+    hipEvent_t ev = nullptr;
+    hipError_t e = inflight_event(p, st, &ev);
+    return e == hipSuccess ? hipEventRecord(ev, st) : e;
 }
 
 // Wait for everything recorded so far.
@@ -387,6 +399,11 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
 
     HIP_TRY(order_after_publish(p, st));
     HIP_TRY(mark(0));
+    // The call's completion event: bound to the dispatch of the call's last
+    // kernel where the launcher can (`bound`), else recorded after it.
+    hipEvent_t done_ev = p->noalloc_done;
+    if (!noalloc) HIP_TRY(inflight_event(p, st, &done_ev));
+    bool bound = false;
     const int dsplits = decode_splits_for(p, n_tokens);
     if (dsplits > 0) {
         // Split-K GEMM with the shrink, then the epilogue, which routes,
@@ -403,6 +420,10 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
         // and leaves its statistics and error counter alone.
         lora::RouteOut out = cs.ro;
         if (pre) out.stats = nullptr, out.err = nullptr;
+        if (!any_separate) {
+            kev.done = done_ev;
+            bound = true;
+        }
         HIP_TRY(lora::launch_decode(a, d, token_adapter_idx, out, st, kev));
         if (!noalloc) {
             p->last_route_T = n_tokens;
@@ -431,6 +452,10 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
         HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
         if (half) {
+            if (!any_separate && kev.stop == nullptr) {
+                kev.done = done_ev;
+                bound = true;
+            }
             HIP_TRY(lora::launch_gemm_tiled(a, cs.split, st, kev));
         } else {
             HIP_TRY(lora::launch_base_gemm(a, st));
@@ -441,12 +466,8 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
     if (ps && ps->staged) HIP_TRY(mark(3));
     if (any_separate) HIP_TRY(half ? lora::launch_expand_sep16(a, st) : lora::launch_expand_separate(a, st));
     HIP_TRY(mark(4));
-    if (noalloc) {
-        HIP_TRY(hipEventRecord(p->noalloc_done, st));
-        p->noalloc_used = true;
-    } else {
-        HIP_TRY(record_inflight(p, st));
-    }
+    if (!bound) HIP_TRY(hipEventRecord(done_ev, st));
+    if (noalloc) p->noalloc_used = true;
     return LORA_OK;
 }
 
@@ -885,12 +906,15 @@ int lora_plan_route(lora_plan plan, lora_pool p, const int32_t *token_adapter_id
     plan->T = -1;
     HIP_TRY(order_after_publish(p, st));
     if (n_tokens > 0) {
-        HIP_TRY(hipMemcpyAsync(plan->idx, token_adapter_idx, static_cast<size_t>(n_tokens) * 4,
-                               hipMemcpyDeviceToDevice, st));
+        // The routing kernel also keeps the plan's copy of the indices (the
+        // small-call path reads them again at every apply).
         lora::RouteOut ro = plan->ro;
         ro.err = p->ro.err;  // invalid tokens counted once, on the routing pool
-        HIP_TRY(lora::launch_route(plan->idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta, ro, st));
-        HIP_TRY(record_inflight(p, st));
+        ro.idx_copy = plan->idx;
+        hipEvent_t pool_ev = nullptr;
+        HIP_TRY(inflight_event(p, st, &pool_ev));
+        HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta, ro,
+                                   st, pool_ev));
     }
     HIP_TRY(hipEventRecord(plan->done, st));
     plan->done_stream = st;

@@ -764,11 +764,12 @@ hipError_t launch_tb(const ApplyArgs &a, const DecodeArgs &d, const int32_t *idx
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const LaunchEvents eev{nullptr, ev.done, nullptr};  // the epilogue ends the call
     switch ((a.R + 15) / 16) {
-        case 1: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 1>), egrid, eblock, 0, st, a, d, idx, out); break;
-        case 2: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 2>), egrid, eblock, 0, st, a, d, idx, out); break;
-        case 3: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 3>), egrid, eblock, 0, st, a, d, idx, out); break;
-        default: hipLaunchKernelGGL((k_decode_epilogue<DT, TB, 4>), egrid, eblock, 0, st, a, d, idx, out); break;
+        case 1: LORA_LAUNCH(eev, (k_decode_epilogue<DT, TB, 1>), egrid, eblock, 0, st, a, d, idx, out); break;
+        case 2: LORA_LAUNCH(eev, (k_decode_epilogue<DT, TB, 2>), egrid, eblock, 0, st, a, d, idx, out); break;
+        case 3: LORA_LAUNCH(eev, (k_decode_epilogue<DT, TB, 3>), egrid, eblock, 0, st, a, d, idx, out); break;
+        default: LORA_LAUNCH(eev, (k_decode_epilogue<DT, TB, 4>), egrid, eblock, 0, st, a, d, idx, out); break;
     }
     return hipGetLastError();
 }

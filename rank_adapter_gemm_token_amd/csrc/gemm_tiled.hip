@@ -558,6 +558,9 @@ hipError_t launch_shape(const ApplyArgs &a, hipStream_t st, LaunchEvents ev) {
 
 template <int DT>
 hipError_t launch_dt(const ApplyArgs &a, const SplitSpace &ws, hipStream_t st, LaunchEvents ev) {
+    // One kernel per call: the completion event, when asked for, is that
+    // kernel's stop event (callers that time the kernel record it themselves).
+    if (ev.done != nullptr && ev.stop == nullptr) ev.stop = ev.done;
     if (a.T >= 2048 && a.d_out % 256 == 0 && a.d_in % 128 == 0) {
         const dim3 grid(a.d_out / 256, (a.T + 255) / 256);
         LORA_LAUNCH(ev, (k_gemm_lds<DT, 256, false>), grid, dim3(512), 0, st, a, SplitArgs{});

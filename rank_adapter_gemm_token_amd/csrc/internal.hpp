@@ -51,6 +51,7 @@ struct RouteOut {
     int32_t *n_tiles;   // [1]
     DevStats *stats;    // [1]   may be null
     unsigned long long *err;  // invalid-token counter, may be null
+    int32_t *idx_copy;  // [T]   copy of the token indices as read (may be null)
 };
 
 // Routing inputs and the epilogue's view of it.
@@ -79,7 +80,7 @@ inline int max_tiles(int T, int S) {
 // ---- launchers (return the launch's hipError_t) ----
 
 hipError_t launch_route(const int32_t *idx, int T, int S, const SlotDev *slots, int R,
-                        int policy, int theta, const RouteOut &out, hipStream_t st);
+                        int policy, int theta, const RouteOut &out, hipStream_t st, hipEvent_t done = nullptr);
 
 // Copy a user adapter into slot `slot` of the slabs, zero-padding rank..R-1.
 // A_user [rank][d_in], B_user [d_out][rank]; slab A [S][R][d_in], slab B
@@ -131,14 +132,20 @@ hipError_t launch_expand_sep16(const ApplyArgs &a, hipStream_t st);
 // Optional timing events of one launch: when `start` is set, the kernel is
 // launched with hipExtLaunchKernelGGL, which records both events from the
 // dispatch itself (the kernel's own device time, no inter-launch gap).
+// Events bound to a launch's dispatch (hipExtLaunchKernelGGL): start and stop
+// time one kernel; `done`, when set, is recorded by the completion of the
+// launcher's last kernel, in place of a separate event record after it (a
+// record is one more packet for the command processor, about 1 us of device
+// time between calls on MI355X).
 struct LaunchEvents {
     hipEvent_t start = nullptr;
     hipEvent_t stop = nullptr;
+    hipEvent_t done = nullptr;
 };
 
 #define LORA_LAUNCH(ev, kernel, grid, block, shmem, st, ...)                                             \
     do {                                                                                                \
-        if ((ev).start)                                                                                 \
+        if ((ev).start || (ev).stop)                                                                    \
             hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, (ev).start, (ev).stop, 0u, __VA_ARGS__); \
         else                                                                                            \
             hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);                            \

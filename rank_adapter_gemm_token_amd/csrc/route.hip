@@ -116,6 +116,11 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     if (T > 0) {
 #pragma unroll
         for (int u = 0; u < IDX_UNROLL; ++u) vi[u] = idx[min(tok(u), T - 1)];
+        if (out.idx_copy != nullptr) {
+#pragma unroll
+            for (int u = 0; u < IDX_UNROLL; ++u)
+                if ((!one_pass || u < nsub) && tok(u) < T) out.idx_copy[tok(u)] = vi[u];
+        }
     }
     for (int k = tid; k < S; k += RT) {
         const SlotDev sd = slots[k];
@@ -185,6 +190,11 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
             if (t0 > 0) {
 #pragma unroll
                 for (int u = 0; u < IDX_UNROLL; ++u) vi[u] = idx[min(t0 + u * RT + tid, T - 1)];
+                if (out.idx_copy != nullptr) {
+#pragma unroll
+                    for (int u = 0; u < IDX_UNROLL; ++u)
+                        if (t0 + u * RT + tid < T) out.idx_copy[t0 + u * RT + tid] = vi[u];
+                }
             }
 #pragma unroll
             for (int u = 0; u < IDX_UNROLL; ++u) {
@@ -362,8 +372,9 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
 }  // namespace
 
 hipError_t launch_route(const int32_t *idx, int T, int S, const SlotDev *slots, int R, int policy,
-                        int theta, const RouteOut &out, hipStream_t st) {
-    hipLaunchKernelGGL(k_route, dim3(1), dim3(RT), 0, st, idx, T, S, slots, R, policy, theta, out);
+                        int theta, const RouteOut &out, hipStream_t st, hipEvent_t done) {
+    LORA_LAUNCH((LaunchEvents{nullptr, done}), k_route, dim3(1), dim3(RT), 0, st, idx, T, S, slots, R, policy, theta,
+                out);
     return hipGetLastError();
 }
 
