@@ -390,18 +390,66 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
         // (s * h of its rows of mode `want`) is formed once per rank step and
         // masked to one bucket's rows per product; a bucket's slot, mode and
         // rank come from the row facts of one of its rows (a ballot per
-        // block), so a batch costs one round of loads.  The B loads are
-        // unconditional (a bucket left out reads slot 0's B and is not
-        // multiplied): conditional loads make the compiler wait for every
-        // earlier load before each, one round per bucket.  The loops over
-        // rank steps and batches stay rolled (their code is fetched once).
-        constexpr int NBB = 8;
+        // block).  Two batches are in flight: batch k + 1's B loads are
+        // issued before batch k's products, so a wave of many short buckets
+        // waits for about one round of loads instead of one per batch.  The B
+        // loads are unconditional (a bucket left out, or a batch past the
+        // run, reads slot 0's B and is not multiplied): the wait before a
+        // batch's products then always counts the next batch's loads alone.
+        // The loops over rank steps and batch pairs stay rolled (their code
+        // is fetched once).
+        constexpr int NBB = 4;
         const int last_row = min(rows_end, p0 + TB * 16) - 1 - p0;  // >= 0: p0 < rows_end
         const int g_lo = uniform(f.g[0]);
         int g_hi = g_lo;
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
             if (tb == last_row / 16) g_hi = __builtin_amdgcn_readlane(f.g[tb], last_row % 16);
+        struct Batch {
+            int keys[NBB];
+            bool use[NBB];
+            uint32_t blocks[NBB];  // bit tb: block tb holds rows of the bucket
+        };
+        auto describe = [&](int gb, int js, Batch &bt) {
+#pragma unroll
+            for (int b = 0; b < NBB; ++b) {
+                const int gg = gb + b;
+                uint32_t bl = 0;
+                int key = a.S, mode = SEG_NONE, rk = 0;
+#pragma unroll
+                for (int tb = TB - 1; tb >= 0; --tb) {
+                    const unsigned long long m = __ballot(f.g[tb] == gg) & 0xFFFFull;
+                    if (m != 0) {
+                        const int l0 = __ffsll(static_cast<long long>(m)) - 1;
+                        bl |= 1u << tb;
+                        key = __builtin_amdgcn_readlane(f.key[tb], l0);
+                        mode = __builtin_amdgcn_readlane(f.mode[tb], l0);
+                        rk = __builtin_amdgcn_readlane(f.rank[tb], l0);
+                    }
+                }
+                bt.use[b] = gg <= g_hi && bl != 0 && key < a.S && mode == want && js * 32 < rk;
+                bt.keys[b] = key;
+                bt.blocks[b] = bl;
+            }
+        };
+        auto issue = [&](const Batch &bt, int js, V (&bf)[NBB][WC]) {
+#pragma unroll
+            for (int b = 0; b < NBB; ++b) load_b(bt.use[b] ? bt.keys[b] : 0, js, bf[b]);
+        };
+        auto multiply = [&](int gb, const Batch &bt, const V (&hq)[TB], const V (&bf)[NBB][WC]) {
+#pragma unroll
+            for (int b = 0; b < NBB; ++b) {
+                if (!bt.use[b]) continue;
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    if ((bt.blocks[b] >> tb) & 1u) {
+                        const V h = f.g[tb] == gb + b ? hq[tb] : zero8<V>();
+#pragma unroll
+                        for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(h, bf[b][wc], acc[tb][wc]);
+                    }
+                }
+            }
+        };
 #pragma nounroll
         for (int js = 0; js < JM; ++js) {
             if (js * 32 >= Rp) break;
@@ -412,46 +460,19 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
                 if (p0 + tb * 16 < rows_end) load_h(tb, js, hv);
                 hq[tb] = make_h(tb, js, -1, hv);
             }
+            Batch ba, bb;
+            V fa[NBB][WC], fb[NBB][WC];
+            describe(g_lo, js, ba);
+            issue(ba, js, fa);
 #pragma nounroll
-            for (int gb = g_lo; gb <= g_hi; gb += NBB) {
-                int keys[NBB];
-                bool use[NBB];
-                uint32_t blocks[NBB];  // bit tb: block tb holds rows of the bucket
-#pragma unroll
-                for (int b = 0; b < NBB; ++b) {
-                    const int gg = gb + b;
-                    uint32_t bl = 0;
-                    int key = a.S, mode = SEG_NONE, rk = 0;
-#pragma unroll
-                    for (int tb = TB - 1; tb >= 0; --tb) {
-                        const unsigned long long m = __ballot(f.g[tb] == gg) & 0xFFFFull;
-                        if (m != 0) {
-                            const int l0 = __ffsll(static_cast<long long>(m)) - 1;
-                            bl |= 1u << tb;
-                            key = __builtin_amdgcn_readlane(f.key[tb], l0);
-                            mode = __builtin_amdgcn_readlane(f.mode[tb], l0);
-                            rk = __builtin_amdgcn_readlane(f.rank[tb], l0);
-                        }
-                    }
-                    use[b] = gg <= g_hi && bl != 0 && key < a.S && mode == want && js * 32 < rk;
-                    keys[b] = key;
-                    blocks[b] = bl;
-                }
-                V bf[NBB][WC];
-#pragma unroll
-                for (int b = 0; b < NBB; ++b) load_b(use[b] ? keys[b] : 0, js, bf[b]);
-#pragma unroll
-                for (int b = 0; b < NBB; ++b) {
-                    if (!use[b]) continue;
-#pragma unroll
-                    for (int tb = 0; tb < TB; ++tb) {
-                        if ((blocks[b] >> tb) & 1u) {
-                            const V h = f.g[tb] == gb + b ? hq[tb] : zero8<V>();
-#pragma unroll
-                            for (int wc = 0; wc < WC; ++wc) acc[tb][wc] = E::mfma(h, bf[b][wc], acc[tb][wc]);
-                        }
-                    }
-                }
+            for (int gb = g_lo; gb <= g_hi; gb += 2 * NBB) {
+                describe(gb + NBB, js, bb);
+                issue(bb, js, fb);
+                multiply(gb, ba, hq, fa);
+                if (gb + NBB > g_hi) break;
+                describe(gb + 2 * NBB, js, ba);
+                issue(ba, js, fa);
+                multiply(gb + NBB, bb, hq, fb);
             }
         }
         return;
