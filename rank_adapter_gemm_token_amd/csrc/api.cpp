@@ -331,7 +331,8 @@ size_t carve_call(lora_pool p, int n_tokens, char *base, CallSpace *cs) {
         h_parts = static_cast<size_t>(dsplits);
         part_floats = static_cast<size_t>(dsplits) * lora::decode_token_blocks(n_tokens) * 16 * p->d_out;
     } else if (p->esz == 2) {
-        h_parts = static_cast<size_t>(lora::tiled_h_parts(p->d_in, p->Rp, lora::max_tiles(n_tokens, p->S), n_tokens));
+        h_parts = static_cast<size_t>(
+            lora::tiled_call_h_parts(n_tokens, p->d_in, p->d_out, p->Rp, lora::max_tiles(n_tokens, p->S)));
         part_floats = lora::tiled_part_bytes(n_tokens, p->d_in, p->d_out) / 4;
     }
     const size_t o_h = take(h_parts * T * p->Rp * 4);
@@ -353,7 +354,8 @@ size_t carve_call(lora_pool p, int n_tokens, char *base, CallSpace *cs) {
         cs->part = reinterpret_cast<float *>(base + o_part);
         // The split counters sit in the scratch's own zeroed block (they are
         // back at 0 after every call).
-        cs->split = lora::SplitSpace{cs->part, lora::scratch_split_counters(p->device), lora::MAX_SPLIT_TILES};
+        unsigned *cnt = lora::scratch_split_counters(p->device);
+        cs->split = lora::SplitSpace{cs->part, cnt, lora::MAX_SPLIT_TILES, cnt + lora::MAX_SPLIT_TILES};
     }
     return off;
 }
@@ -440,16 +442,24 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
             }
         }
         HIP_TRY(mark(1));
-        if (half) {
-            // k parts of the shrink; the grouped shrink adds them into part 0
-            // itself (on the counters the split tiles also use, in stream
-            // order, each kernel leaving them at 0), so its consumers read one.
-            const int parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound, n_tokens);
-            a.shrink_g = lora::shrink_group(n_tokens, a.tiles_bound, cs.split.max_tiles);
-            a.shrink_parts = parts;
-            a.h_parts = a.shrink_g > 1 ? 1 : parts;
+        // Split calls whose GEMM grid is one round run the shrink inside the
+        // GEMM launch (its k parts are the plan's).
+        const int fused_parts = half ? lora::tiled_plan(n_tokens, p->d_in, p->d_out).fuse_parts : 0;
+        if (fused_parts > 0) {
+            a.shrink_parts = fused_parts;
+            a.h_parts = fused_parts;
+        } else {
+            if (half) {
+                // k parts of the shrink; the grouped shrink adds them into part 0
+                // itself (on the counters the split tiles also use, in stream
+                // order, each kernel leaving them at 0), so its consumers read one.
+                const int parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound, n_tokens);
+                a.shrink_g = lora::shrink_group(n_tokens, a.tiles_bound, cs.split.max_tiles);
+                a.shrink_parts = parts;
+                a.h_parts = a.shrink_g > 1 ? 1 : parts;
+            }
+            HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         }
-        HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
         if (half) {
             if (!any_separate && kev.stop == nullptr) {
@@ -473,7 +483,8 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
 
 // The pool's own workspace.
 CallSpace pool_space(lora_pool p) {
-    return CallSpace{p->ro, p->h, p->part, lora::SplitSpace{p->part, p->split_cnt, p->split_tiles}};
+    return CallSpace{p->ro, p->h, p->part,
+                     lora::SplitSpace{p->part, p->split_cnt, p->split_tiles, p->split_cnt + p->split_tiles}};
 }
 
 // Host-side checks shared by lora_apply and lora_apply_noalloc.
@@ -591,12 +602,12 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
     // per k split of their GEMM, [splits][T][Rp], and the splits' partial
     // sums [splits][T rounded up to 16 .. 64][d_out].
     const int dec_splits = (esz == 2) ? lora::decode_splits(static_cast<int>(dec_T), d_in, d_out) : 0;
-    // Calls on the tiled path keep tiled_h_parts parts, [parts][T][Rp].
+    // Calls on the tiled path keep tiled_call_h_parts parts, [parts][T][Rp].
     size_t h_rows = std::max(T, static_cast<size_t>(dec_splits) * dec_T);
     if (esz == 2)
         for (int t = 1; t <= max_tokens; ++t)
             h_rows = std::max(h_rows, static_cast<size_t>(t) *
-                                          lora::tiled_h_parts(d_in, Rp, lora::max_tiles(t, n_slots), t));
+                                          lora::tiled_call_h_parts(t, d_in, d_out, Rp, lora::max_tiles(t, n_slots)));
     const size_t o_h = take(h_rows * Rp * 4);
     const size_t dec_rows = static_cast<size_t>(lora::decode_token_blocks(static_cast<int>(dec_T))) * 16;
     // Split tiles of calls of 65 .. 2047 tokens: the largest partial-sum
@@ -615,7 +626,8 @@ int lora_pool_create(int d_in, int d_out, int max_rank, int n_slots, int max_tok
                                                     lora::SHRINK_G);
     }
     const size_t o_part = take(std::max(static_cast<size_t>(dec_splits) * dec_rows * d_out * 4, tiled_part));
-    const size_t o_cnt = take(static_cast<size_t>(split_tiles) * 4);
+    // ... and the fused shrink's two counters after them.
+    const size_t o_cnt = take(static_cast<size_t>(split_tiles + 2) * 4);
     const size_t ws_bytes = off;
 
     e = hipMalloc(&p->A_slab, a_bytes);

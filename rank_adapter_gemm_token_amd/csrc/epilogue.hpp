@@ -48,7 +48,9 @@ __device__ __forceinline__ void store_h(float *p, float v) {
         *p = v;
 }
 
-template <int DT, int RB, int NWV, bool SC1 = false>
+// UO (when > 0) sets U, the k steps a wave keeps in flight, to UO / RB in
+// place of the default for RB (the same registers for every RB).
+template <int DT, int RB, int NWV, bool SC1 = false, int UO = 0>
 __device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row0, int rows,
                                             const int32_t *perm, int part, u32x4_t *lds) {
     using E = Elem<DT>;
@@ -84,7 +86,7 @@ __device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row
 #pragma unroll
     for (int cb = 0; cb < RB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int U = RB == 1 ? 16 : RB == 2 ? 8 : 4;  // k steps whose loads are all in flight together
+    constexpr int U = UO > 0 ? (UO / RB > 0 ? UO / RB : 1) : RB == 1 ? 16 : RB == 2 ? 8 : 4;  // k steps in flight together
     for (int k0 = kb; k0 < ke; k0 += U) {
         V xa[U];
         V b[U][RB];
@@ -130,7 +132,7 @@ __device__ __forceinline__ void shrink_unit(const ApplyArgs &a, int key, int row
 }
 
 // shrink_unit for tile `tile` of the routing in global memory.
-template <int DT, int RB, int NWV, bool SC1 = false>
+template <int DT, int RB, int NWV, bool SC1 = false, int UO = 0>
 __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int part, u32x4_t *lds) {
     if (tile >= uniform(*a.rv.n_tiles)) return;
     const int tw = a.rv.tiles[2 * tile];
@@ -141,27 +143,43 @@ __device__ __forceinline__ void shrink_role(const ApplyArgs &a, int tile, int pa
     const int rows = min(TILE_ROWS, end - row0);
     // Rank blocks that hold the slot's true rank (the tile carries it).
     const int nrb = uniform(min(RB, (tile_rank(tw) + 15) / 16));
-    if (RB >= 4 && nrb == 4) shrink_unit<DT, (RB >= 4 ? 4 : 1), NWV, SC1>(a, key, row0, rows, a.rv.perm, part, lds);
-    else if (RB >= 3 && nrb == 3) shrink_unit<DT, (RB >= 3 ? 3 : 1), NWV, SC1>(a, key, row0, rows, a.rv.perm, part, lds);
-    else if (RB >= 2 && nrb == 2) shrink_unit<DT, (RB >= 2 ? 2 : 1), NWV, SC1>(a, key, row0, rows, a.rv.perm, part, lds);
-    else shrink_unit<DT, 1, NWV, SC1>(a, key, row0, rows, a.rv.perm, part, lds);
+    if (RB >= 4 && nrb == 4) shrink_unit<DT, (RB >= 4 ? 4 : 1), NWV, SC1, UO>(a, key, row0, rows, a.rv.perm, part, lds);
+    else if (RB >= 3 && nrb == 3) shrink_unit<DT, (RB >= 3 ? 3 : 1), NWV, SC1, UO>(a, key, row0, rows, a.rv.perm, part, lds);
+    else if (RB >= 2 && nrb == 2) shrink_unit<DT, (RB >= 2 ? 2 : 1), NWV, SC1, UO>(a, key, row0, rows, a.rv.perm, part, lds);
+    else shrink_unit<DT, 1, NWV, SC1, UO>(a, key, row0, rows, a.rv.perm, part, lds);
 }
 
 // h[p][j .. j+7] summed over the shrink's k parts in order (p: the h row,
 // a sorted position or a token).  The first HP parts' loads are all in flight
 // before the first add; parts beyond HP (if any) are added one at a time.
-template <int HP>
+// COH: h was written by other workgroups of the same launch (agent-coherent
+// stores), so it is read with agent-coherent loads, which no stale line of
+// this XCD's L2 can serve.
+template <int HP, bool COH = false>
 __device__ __forceinline__ void load_h8(const ApplyArgs &a, int p, int j, float (&hv)[8]) {
     const size_t stride = static_cast<size_t>(a.T) * a.R;
     const float *hp = a.h + static_cast<size_t>(p) * a.R + j;
     const int np = uniform(a.h_parts);
     float4 v[HP][2];
+    if constexpr (COH) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.h, static_cast<uint32_t>(np * stride * 4));
+        const uint32_t off = static_cast<uint32_t>((static_cast<size_t>(p) * a.R + j) * 4);
 #pragma unroll
-    for (int q = 0; q < HP; ++q) {
-        if (q < np) {
-            const float4 *hq = reinterpret_cast<const float4 *>(hp + q * stride);
-            v[q][0] = hq[0];
-            v[q][1] = hq[1];
+        for (int q = 0; q < HP; ++q) {
+            if (q < np) {
+                const uint32_t qo = static_cast<uint32_t>(q * stride * 4);
+                v[q][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, qo, CPOL_SC1));
+                v[q][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, qo, CPOL_SC1));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < HP; ++q) {
+            if (q < np) {
+                const float4 *hq = reinterpret_cast<const float4 *>(hp + q * stride);
+                v[q][0] = hq[0];
+                v[q][1] = hq[1];
+            }
         }
     }
     float4 h0 = v[0][0], h1 = v[0][1];
@@ -172,6 +190,7 @@ __device__ __forceinline__ void load_h8(const ApplyArgs &a, int p, int j, float 
 #pragma unroll
     for (int q = 1; q < HP; ++q)
         if (q < np) add(v[q][0], v[q][1]);
+    static_assert(!COH || HP == MAX_HPARTS, "coherent h reads keep every part in flight");
     for (int q = HP; q < np; ++q) {
         const float4 *hq = reinterpret_cast<const float4 *>(hp + q * stride);
         add(hq[0], hq[1]);
@@ -261,7 +280,7 @@ __device__ __forceinline__ void prefetch_h1(const ApplyArgs &a, int p0, int rows
 // usual case for long buckets) its B fragments are loaded once; otherwise
 // each block meets its buckets one at a time (rows are sorted, so a bucket
 // is a run of lanes), one round of B loads per bucket.
-template <int DT, int TB, int WC, int HP = MAX_HPARTS>
+template <int DT, int TB, int WC, int HP = MAX_HPARTS, bool COH = false>
 __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int rows_end, int n0, int want,
                                                  const RowFacts<TB> &f, f32x4_t (&acc)[TB][WC],
                                                  const float (*hpre)[8] = nullptr) {
@@ -292,7 +311,7 @@ __device__ __forceinline__ void lora_expand_mfma(const ApplyArgs &a, int p0, int
             return;
         }
         const int hrow = a.h_by_token ? f.tok[tb] : min(p0 + tb * 16 + r, rows_end - 1);
-        load_h8<HP>(a, hrow, min(js * 32 + 8 * kq, Rp - 8), hv);
+        load_h8<HP, COH>(a, hrow, min(js * 32 + 8 * kq, Rp - 8), hv);
     };
     // H operand of block tb, rank step js, for bucket gg (-1: any bucket of
     // mode `want`).

@@ -214,8 +214,27 @@ __device__ __forceinline__ void xcd_tile_order(int nx, int ny, int id, int &tm, 
     tn = r / rows;
 }
 
-template <int DT, int BN, bool SPLIT>
+// FS (split calls whose tiles leave CUs idle): the LoRA shrink runs inside
+// this launch instead of a launch of its own, on the `shrink_wgs` workgroups
+// after the tiles' contributors.  h is cut into units u = (bucket tile u / P,
+// k part u % P), P = a.h_parts; the shrink workgroups take units round-robin,
+// each an 8-wave shrink_role with agent-coherent h stores, and count the
+// units they finished on sp.sync[0] once those stores are complete.  The
+// consumers of h (the LoRA workgroups before their expand, else the last
+// contributor of a tile before its tail expand) wait until the count reaches
+// n_tiles x P, then read h with agent-coherent loads.  The wait is bounded: a
+// consumer that does not see the count in time (only possible when the grid
+// is not all resident at once) computes every unit itself with the same code
+// -- the same h bits -- and goes on.  Every workgroup counts itself on
+// sp.sync[1] when it is done with h; the last one resets both counters to 0
+// for the next call.  Shrink workgroups never wait, so the grid drains in any
+// residency.
+constexpr int FS_U = 8;                 // k steps a shrink wave keeps in flight
+constexpr int FS_SPIN_MAX = 1 << 17;    // polls of the unit count (~0.1-0.3 s)
+
+template <int DT, int BN, bool SPLIT, bool FS = false>
 __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
+    static_assert(!FS || SPLIT, "the fused shrink serves split calls");
     using E = Elem<DT>;
     using V = typename E::vec8;
     constexpr int BM = 256;
@@ -237,6 +256,7 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
     // of the invalid bucket), for the epilogue's stores.
     __shared__ int rowtok[SPLIT ? 1 : BM];
     __shared__ int last_split;
+    __shared__ int h_late;
 
     const int wave = uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -249,6 +269,63 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
     // plan has one (contributor 0 of the tile, numbered z = splits).
     const int nc = SPLIT ? sp.splits + sp.lora_wg : 1;
     bool lora_role = false;
+
+    // Fused shrink (FS): this workgroup's units, then their count.
+    auto produce = [&](int j, int np, u32x4_t *scratch) __attribute__((always_inline)) {
+        const int P = uniform(a.h_parts);
+        const int need = uniform(*a.rv.n_tiles) * P;
+        int done = 0;
+        for (int u = j; u < need; u += np) {
+            const int t = u / P;
+            shrink_role<DT, 4, 8, true, FS_U>(a, t, u - t * P, scratch);
+            __syncthreads();  // wave 0's reads of the scratch are done before the next unit's writes
+            ++done;
+        }
+        if (done > 0 && threadIdx.x == 0) {
+            // (Thread 0 is in wave 0, which made the h stores.)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __hip_atomic_fetch_add(sp.sync, static_cast<unsigned>(done), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+    };
+    // Fused shrink: wait (bounded) until every unit is counted; past the
+    // bound, compute them all here.  Every wave of the workgroup calls it.
+    auto wait_h = [&](u32x4_t *scratch) __attribute__((always_inline)) {
+        const int P = uniform(a.h_parts);
+        const int need = uniform(*a.rv.n_tiles) * P;
+        if (threadIdx.x == 0) {
+            int spins = 0;
+            while (__hip_atomic_load(sp.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                       static_cast<unsigned>(need) &&
+                   spins < FS_SPIN_MAX) {
+                __builtin_amdgcn_s_sleep(2);
+                ++spins;
+            }
+            h_late = spins >= FS_SPIN_MAX;
+        }
+        __syncthreads();
+        if (uniform(h_late)) {
+            for (int u = 0; u < need; ++u) {
+                const int t = u / P;
+                shrink_role<DT, 4, 8, true, FS_U>(a, t, u - t * P, scratch);
+                __syncthreads();
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    };
+    // Fused shrink: this workgroup is done with h (thread 0, once).
+    auto depart = [&]() __attribute__((always_inline)) {
+        if (threadIdx.x == 0) {
+            const unsigned old =
+                __hip_atomic_fetch_add(sp.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old == gridDim.x - 1) {
+                __hip_atomic_store(sp.sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sp.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
+
     if constexpr (SPLIT) {
         // Workgroup id -> (tile, contributor): ids are dealt to the XCDs
         // round-robin (id mod 8), so when 8 divides the grid, XCD k takes the
@@ -256,6 +333,14 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
         // contributors follow one another.
         const int n = sp.tiles * nc;
         const int id = static_cast<int>(blockIdx.x);
+        if constexpr (FS) {
+            if (id >= n) {
+                // A shrink workgroup (after the tiles' contributors).
+                produce(id - n, sp.shrink_wgs, lds0);
+                depart();
+                return;
+            }
+        }
         const int q = uniform((n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id);
         tile = uniform(q / nc);
         const int j = uniform(q - tile * nc);
@@ -416,6 +501,7 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
     const int nst = s_end - s_beg;
     if (nst == 0) {
         // (The LoRA workgroup of a split tile.)
+        if constexpr (FS) wait_h(lds0);
     } else if (NBUF == 2) {
         issue(s_beg, lds0);
         if constexpr (!SPLIT) lora_prologue();
@@ -450,7 +536,7 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
     // The epilogue's addresses depend on pw, which the compiler may not
     // compute before the loop (keeps them from being hoisted and held in
     // registers across it).
-    int pw = m0 + wm * TB * 16;
+    int pw = uniform(m0 + wm * TB * 16);
     asm volatile("" : "+s"(pw));
     const int nw = n0 + wn * WC * 16;
     if constexpr (!SPLIT) {
@@ -468,10 +554,11 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
             // The LoRA workgroup: the tile's fused expand, s * h . B^T, from
             // zero (its main loop took no k stage).
             row_facts<TB>(a, pw, a.T, f);
-            lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, f, acc);
+            lora_expand_mfma<DT, TB, WC, MAX_HPARTS, FS>(a, pw, a.T, nw, SEG_FUSED, f, acc);
         }
         if (nc == 1) {
-            if (!rows_live) return;
+            if constexpr (FS) wait_h(lds0);  // the tile's expand follows (no LoRA workgroup)
+            if (!rows_live) return;  // (never wave 0, which departs at the end)
             row_facts_begin<TB>(a, pw, a.T, f);
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
@@ -505,6 +592,10 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
                 last_split = last;
             }
             __syncthreads();
+            if constexpr (FS) {
+                if (!uniform(last_split)) depart();
+                else if (!sp.lora_wg) wait_h(lds0);
+            }
             if (!last_split || !rows_live) return;
             // The last contributor of the tile: the rows' routing facts and
             // the other contributors' fragments requested together, NZ a
@@ -544,8 +635,9 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
             }
         }
         if (!lora_role) row_facts_end<TB>(a, pw, a.T, f);
-        if (!sp.lora_wg) lora_expand_mfma<DT, TB, WC>(a, pw, a.T, nw, SEG_FUSED, f, sum);
+        if (!sp.lora_wg) lora_expand_mfma<DT, TB, WC, MAX_HPARTS, FS>(a, pw, a.T, nw, SEG_FUSED, f, sum);
         store_rows<DT, TB, WC>(a, pw, a.T, nw, f, sum);
+        if constexpr (FS) depart();
     }
 }
 
@@ -575,11 +667,22 @@ hipError_t launch_dt(const ApplyArgs &a, const SplitSpace &ws, hipStream_t st, L
         sp.tiles = sp.tiles_x * ((a.T + 255) / 256);
         sp.part = ws.part;
         sp.cnt = ws.cnt;
+        sp.shrink_wgs = tp.shrink_wgs;
+        sp.sync = ws.sync;
         // The workspace was sized with tiled_part_bytes / tiled_split_tiles.
         const int nc = tp.splits + tp.lora_wg;
         if (nc > 1 && (ws.part == nullptr || ws.cnt == nullptr || sp.tiles > ws.max_tiles))
             return hipErrorInvalidValue;
         if (tp.bn != 64 || tp.splits > MAX_TSPLIT || tp.lora_wg > 1) return hipErrorInvalidValue;
+        if (tp.fuse_parts > 0) {
+            // The caller set h_parts to the plan's and launched no shrink.
+            if (ws.sync == nullptr || tp.shrink_wgs <= 0 || a.h_parts != tp.fuse_parts ||
+                a.shrink_parts != tp.fuse_parts || a.h_by_token != 0 || a.R > 64)
+                return hipErrorInvalidValue;
+            const dim3 grid(sp.tiles * nc + tp.shrink_wgs);
+            LORA_LAUNCH(ev, (k_gemm_lds<DT, 64, true, true>), grid, dim3(512), 0, st, a, sp);
+            return hipGetLastError();
+        }
         const dim3 grid(sp.tiles * nc);
         LORA_LAUNCH(ev, (k_gemm_lds<DT, 64, true>), grid, dim3(512), 0, st, a, sp);
         return hipGetLastError();
@@ -606,7 +709,7 @@ TiledPlan tiled_plan(int T, int d_in, int d_out) {
     // round.  (The same model prefers 64- over 128-column tiles at every T
     // here: the wider tile needs more splits for the same grid.)  splits 0:
     // not this path.
-    if (T <= DECODE_MAX_T || T >= 2048 || d_out % 64 != 0 || d_in % 128 != 0) return TiledPlan{0, 0, 0};
+    if (T <= DECODE_MAX_T || T >= 2048 || d_out % 64 != 0 || d_in % 128 != 0) return TiledPlan{0, 0, 0, 0, 0};
     const int bn = 64;
     const int row_tiles = (T + 255) / 256;
     const double rows = T < 256 ? static_cast<double>((T + 63) / 64 * 64) : 256.0;  // x rows a tile loads
@@ -614,7 +717,7 @@ TiledPlan tiled_plan(int T, int d_in, int d_out) {
     const double w_s = static_cast<double>(d_in) * d_out * 2 / 5e12;
     const double cu_mfma = 2.5e15 / 256 * 0.6;
     const int tiles = d_out / bn * row_tiles;
-    TiledPlan best{0, 0, 0};
+    TiledPlan best{0, 0, 0, 0, 0};
     double best_t = 0.0;
     int best_wgs = 0;
     for (int s = 1; s <= MAX_TSPLIT; ++s) {
@@ -643,13 +746,30 @@ TiledPlan tiled_plan(int T, int d_in, int d_out) {
             const bool better = best.splits == 0 || (wgs > best_wgs ? t <= best_t * 1.01 : t < best_t * 0.99) ||
                                 (wgs == best_wgs && t < best_t);
             if (better) {
-                best = TiledPlan{bn, s, lw};
+                best = TiledPlan{bn, s, lw, 0, 0};
                 best_t = t;
                 best_wgs = wgs;
             }
         }
     }
+    // The shrink joins the launch on the CUs the tiles leave idle (at least
+    // 64): its k parts give each shrink wave at most FS_U k steps (one round
+    // of loads).  With every CU taken by a tile, the shrink stays a launch of
+    // its own: measured on MI355X, shrink units in the tile workgroups'
+    // prologues delayed their main loops and the LoRA workgroups' expand by
+    // more than the launch they saved (256 tokens, 4096 x 4096: GEMM 27 ->
+    // 39 us, call 38.2 -> 43.6 us).
+    const int wgs = tiles * (best.splits + best.lora_wg);
+    if (best.splits > 0 && 256 - wgs >= 64) {
+        best.fuse_parts = std::min(MAX_HPARTS, std::max(1, (d_in / 32 + 8 * FS_U - 1) / (8 * FS_U)));
+        best.shrink_wgs = 256 - wgs;
+    }
     return best;
+}
+
+int tiled_call_h_parts(int T, int d_in, int d_out, int R, int tiles) {
+    const TiledPlan tp = tiled_plan(T, d_in, d_out);
+    return tp.fuse_parts > 0 ? tp.fuse_parts : tiled_h_parts(d_in, R, tiles, T);
 }
 
 size_t tiled_part_bytes(int T, int d_in, int d_out) {

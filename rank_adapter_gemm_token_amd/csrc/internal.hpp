@@ -183,18 +183,27 @@ int decode_token_blocks(int T);
 // a tile resets its counter).
 constexpr int MAX_TSPLIT = 8;
 constexpr int MAX_SPLIT_TILES = 16384;
+// When the tiles leave at least 64 CUs idle, the split GEMM also runs the
+// shrink, on `shrink_wgs` extra workgroups (fuse_parts = the k parts P of h
+// it computes; 0: a shrink launch precedes the GEMM).
 struct TiledPlan {
     int bn;
     int splits;
     int lora_wg;         // 1: a LoRA workgroup per tile computes the fused expand
+    int fuse_parts;
+    int shrink_wgs;
 };
 TiledPlan tiled_plan(int T, int d_in, int d_out);
 size_t tiled_part_bytes(int T, int d_in, int d_out);
 int tiled_split_tiles(int T, int d_in, int d_out);
+// k parts of h for a call of T tokens on the tiled path: the fused shrink's,
+// or tiled_h_parts (tiles: the call's bound of bucket tiles).
+int tiled_call_h_parts(int T, int d_in, int d_out, int R, int tiles);
 struct SplitSpace {
     float *part = nullptr;
     unsigned *cnt = nullptr;
     int max_tiles = 0;   // counters available at cnt
+    unsigned *sync = nullptr;  // [2] the fused shrink's counters (0 between calls)
 };
 struct SplitArgs {
     int splits;
@@ -203,6 +212,8 @@ struct SplitArgs {
     int tiles_x;         // column tiles
     float *part;
     unsigned *cnt;
+    int shrink_wgs;      // fused shrink: shrink workgroups after the tiles' contributors
+    unsigned *sync;      // fused shrink: [units counted, workgroups done]
 };
 hipError_t launch_gemm_tiled(const ApplyArgs &a, const SplitSpace &ws, hipStream_t st, LaunchEvents ev = {});
 // The static per-device workspace of lora_apply_noalloc (scratch.hip):
@@ -211,7 +222,9 @@ hipError_t launch_gemm_tiled(const ApplyArgs &a, const SplitSpace &ws, hipStream
 // The array's first SCRATCH_COUNTER_BYTES hold the split tiles' counters
 // (zeroed at set-up, 0 between calls): scratch_split_counters; the per-call
 // workspace is carved from scratch_device_ptr, the rest.
-constexpr size_t SCRATCH_COUNTER_BYTES = static_cast<size_t>(MAX_SPLIT_TILES) * 4;
+// The two counters after the split tiles' are the fused shrink's
+// (SplitSpace::sync); the block stays a multiple of 256 bytes.
+constexpr size_t SCRATCH_COUNTER_BYTES = static_cast<size_t>(MAX_SPLIT_TILES + 64) * 4;
 hipError_t scratch_setup(int device);
 char *scratch_device_ptr(int device);
 unsigned *scratch_split_counters(int device);

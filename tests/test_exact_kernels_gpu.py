@@ -9,10 +9,19 @@ depends on (T, d_in, d_out, dtype) only):
   decode_col  the same, 8 column groups x 16 k splits (narrow output)
   split4      k_gemm_lds<64, split> (65 .. 2047 tokens), 4 tiles x 4 k
               splits summed by the last split of each tile, a 64-row x
-              group past T
+              group past T; the shrink in the same launch, on workgroups
+              after the tiles' (the grid leaves CUs idle)
   split2_rows2  the same, two 256-row tiles, 2 k splits
   split_xcd   the same, 3 tiles x 4 splits (a grid 8 does not divide: a
               tile's splits run on different XCDs)
+  split_tail1 128 tiles x 1 split + 128 shrink workgroups: each tile waits
+              for the shrink before its tail expand
+  split_tail2 96 tiles x 2 splits + 64 shrink workgroups, no LoRA
+              workgroup: the last split of a tile waits before the expand
+  split_lora_nofuse  56 tiles x (3 splits + LoRA workgroup) = 224
+              workgroups: too few idle CUs, the shrink in a launch of its own
+  split_nofuse  384 tiles x 1 split (more than one round of the CUs): the
+              shrink in a launch of its own (grouped tiles, >= 1024 tokens)
   big         k_gemm_lds<256> (>= 2048 tokens, 256-row tiles)
   tiled       k_gemm_tiled (shapes off the 128 grid)
 
@@ -52,6 +61,10 @@ SHAPES = {
     "split4": (130, 1024, 256, 9, 16),      # 4 tiles x 4 splits
     "split2_rows2": (300, 1024, 512, 9, 32),  # 16 tiles (2 rows) x 2 splits
     "split_xcd": (70, 1024, 192, 6, 16),     # 3 tiles x 4 splits: splits on different XCDs
+    "split_tail1": (300, 1024, 4096, 9, 16),     # 128 tiles x 1 split + 128 shrink workgroups
+    "split_tail2": (700, 2048, 2048, 9, 16),     # 96 tiles x 2 splits + 64 shrink workgroups
+    "split_lora_nofuse": (1600, 2048, 512, 9, 16),  # 56 tiles x (3 + 1), separate shrink
+    "split_nofuse": (1300, 256, 4096, 6, 16),    # 384 tiles: separate (grouped) shrink
     "big": (2048, 256, 256, 12, 64),
     "tiled": (70, 128, 192, 6, 16),
 }
@@ -217,8 +230,9 @@ def test_integer_inputs_exact(shape, dtype, limit, policy):
 
 
 # Decode calls keep partial sums and h in the pool's workspace between the
-# GEMM and its epilogue launch.
-DECODE_SHAPES = ["decode64", "decode5", "decodeS70"]
+# GEMM and its epilogue launch; split calls with the shrink in the GEMM
+# launch count its units on counters that every call leaves at 0.
+DECODE_SHAPES = ["decode64", "decode5", "decodeS70", "split4", "split_tail1", "split_tail2"]
 
 
 @pytest.mark.parametrize("shape", DECODE_SHAPES)
@@ -242,5 +256,46 @@ def test_decode_alternating_inputs(shape):
             assert torch.equal(y.cpu().view(torch.int16), ref[k % 2]), k
         r0, inv0 = reference(p, x0, W, idx0)
         assert_close(outs[0].cpu(), r0, inv0, "f16")
+    finally:
+        p.close()
+
+
+def test_split_calls_of_every_plan_on_one_pool():
+    # One pool, calls whose plans differ (shrink on extra workgroups, on the
+    # tile workgroups with LoRA workgroups or tail consumers, or in its own
+    # launch), in a repeating order on one stream: each call's output equals
+    # its own first result bitwise (a counter left non-zero by one plan would
+    # let the next call's consumers read h before it is complete) and the
+    # oracle within tolerance.
+    d_in, d_out, S, R = 256, 4096, 6, 16
+    rng = np.random.default_rng(21)
+    Ts = [130, 1024, 1300, 300, 1024, 70]
+    p = Pool(d_in, d_out, R, S, max(Ts), "bf16", lora.LORA_MODE_AUTO, 0)
+    try:
+        ads = []
+        for s in range(S):
+            r = int(rng.integers(1, R + 1))
+            ads.append(wl.Adapter(s, s, r, float(2 * r),
+                                  torch.from_numpy(rng.standard_normal((r, d_in)) / np.sqrt(d_in)).bfloat16(),
+                                  torch.from_numpy(rng.standard_normal((d_out, r)) * 0.1).bfloat16()))
+        p.register_all(ads)
+        W = torch.from_numpy(rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)).bfloat16()
+        Wd = dev(W)
+        cases = []
+        for T in Ts:
+            x = torch.from_numpy(rng.standard_normal((T, d_in))).bfloat16()
+            idx = torch.from_numpy(rng.integers(-1, S, size=T).astype(np.int32))
+            cases.append((x, idx, dev(x), dev(idx)))
+        first = [p.apply(xd, Wd, idd).cpu().view(torch.int16) for _, _, xd, idd in cases]
+        outs = []
+        for k in range(3 * len(cases)):
+            _, _, xd, idd = cases[k % len(cases)]
+            outs.append(p.apply(xd, Wd, idd))
+        torch.cuda.synchronize()
+        for k, y in enumerate(outs):
+            assert torch.equal(y.cpu().view(torch.int16), first[k % len(cases)]), k
+        for (x, idx, _, _), y in zip(cases, first):
+            ref, inv = reference(p, x, W, idx)
+            assert_close(y.view(torch.bfloat16), ref, inv, "bf16")
     finally:
         p.close()
