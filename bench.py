@@ -270,8 +270,11 @@ def write_counters(workload, fetch_dir, write_dir):
     import csv
     import glob
     kind = workload_kind(workload)
+    # k_gemm_lds<dtype, tile width, split, fused shrink>: the split kernel
+    # (64-wide tiles, with or without the shrink in its launch) or the
+    # 256-wide unsplit one.
     match = {"decode": "k_decode_gemm", "split": "k_gemm_lds<", "big": "k_gemm_lds<"}[kind]
-    must = {"decode": "", "split": ", true>", "big": ", false>"}[kind]
+    must = {"decode": "", "split": ", 64, true", "big": ", 256, false"}[kind]
 
     def read(d, counter):
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -466,8 +469,11 @@ def calibration(dtype):
     """Achievable peaks on this GPU, from the probes in libcalibrate.so: one
     pass of 16-byte non-temporal loads over a 1 GiB buffer (larger than the
     256 MB last-level cache), a register-only loop of 16x16x32 MFMAs in the
-    workload's 16-bit type (fp16 for fp32 workloads), each the best of a few
-    grid sizes; plus a 1 GiB device-to-device torch copy (read + write bytes)."""
+    workload's 16-bit type (fp16 for fp32 workloads), every workgroup
+    re-reading one 2 MiB window that stays in L2 (the L2-to-CU rate that
+    bounds kernels re-streaming an activation block per column tile), each
+    the best of a few grid sizes; plus a 1 GiB device-to-device torch copy
+    (read + write bytes)."""
     import ctypes
     path = os.path.join(ROOT, "rank_adapter_gemm_token_amd", "libcalibrate.so")
     if not os.path.exists(path):
@@ -478,6 +484,8 @@ def calibration(dtype):
     lib.calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     lib.calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.calib_mfma_flops.restype = ctypes.c_double
+    lib.calib_l2read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_void_p]
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -506,6 +514,13 @@ def calibration(dtype):
     dst = torch.empty_like(buf)
     t_copy = per_launch(lambda: dst.copy_(buf), 10)
     del buf, dst
+    win, l2reps = 2 << 20, 4
+    wbuf = torch.ones(win, dtype=torch.uint8, device="cuda")
+    l2 = {}
+    for blocks in (256, 512, 1024):
+        t = per_launch(lambda: check(lib.calib_l2read(wbuf.data_ptr(), win, l2reps, sink.data_ptr(), blocks, sp)), 10)
+        l2[blocks] = blocks * l2reps * win / t / 1e9
+    del wbuf
     bf = 1 if dtype == "bf16" else 0
     iters = 2000
     mfma = {}
@@ -516,9 +531,12 @@ def calibration(dtype):
     return {"read_GBs": max(read.values()), "read_GBs_by_blocks": read,
             "mfma_TFLOPs": max(mfma.values()), "mfma_TFLOPs_by_blocks": mfma,
             "copy_GBs": 2 * n / t_copy / 1e9,
+            "l2_read_GBs": max(l2.values()), "l2_read_GBs_by_blocks": l2,
             "what": "libcalibrate.so: 1 GiB read once (16-byte non-temporal loads, grid-stride), "
-                    "register-only 16x16x32 %s MFMA loop (8 chains per wave); 1 GiB torch copy_ "
-                    "(read+write bytes); 10 (5) timed launches after one untimed" % ("bf16" if bf else "f16")}
+                    "register-only 16x16x32 %s MFMA loop (8 chains per wave), every workgroup reading "
+                    "one 2 MiB window 4 times (16-byte loads, L2-resident; bytes the CUs take in); "
+                    "1 GiB torch copy_ (read+write bytes); 10 (5) timed launches after one untimed"
+                    % ("bf16" if bf else "f16")}
 
 
 def single_call_latency(L, steps, n):

@@ -11,6 +11,11 @@
 //   calib_mfma  runs a register-only loop of v_mfma_f32_16x16x32_{f16,bf16}
 //               (eight independent accumulators per wave); its FLOPs over
 //               its time are the achievable dense 16-bit MFMA rate.
+//   calib_l2read  has every workgroup stream the same small window (a few
+//               MiB, resident in each XCD's L2 after the first pass) with
+//               16-byte loads, the way a GEMM's column tiles all re-read one
+//               activation block; the bytes the CUs take in over its time
+//               are the achievable L2-to-CU rate.
 //
 // Both write one word only when their data-dependent result hits a value it
 // never takes, so the work cannot be dropped and nothing else is written.
@@ -43,6 +48,31 @@ __global__ __launch_bounds__(kThreads) void k_read(const u32x4 *__restrict__ p, 
         for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
     }
     for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+    const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (r == 0x9e3779b9u) sink[0] = r;
+}
+
+// Workgroup b reads the window `reps` times, starting b * 64 KiB in (mod the
+// window) so that the workgroups spread over the L2 channels; each pass is
+// grid-stride over the workgroup's lanes, four loads in flight per lane.
+__global__ __launch_bounds__(kThreads) void k_l2read(const u32x4 *__restrict__ p, size_t win16, int reps,
+                                                     uint32_t *sink) {
+    const size_t start = (static_cast<size_t>(blockIdx.x) * 4096) % win16;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int rep = 0; rep < reps; ++rep) {
+        for (size_t i = threadIdx.x; i < win16; i += kUnroll * kThreads) {
+            u32x4 v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                size_t j = start + i + u * kThreads;
+                j = j >= win16 ? j - win16 : j;
+                j = j >= win16 ? j - win16 : j;
+                v[u] = p[j];
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+        }
+    }
     const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
     if (r == 0x9e3779b9u) sink[0] = r;
 }
@@ -86,6 +116,16 @@ int calib_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, void *
     if (buf == nullptr || sink == nullptr || blocks < 1 || bytes % 16 != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_read, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4 *>(buf), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+// `blocks` workgroups each read the `bytes` (a multiple of 16 * 1024) at `buf`
+// `reps` times: blocks * reps * bytes bytes taken in by the CUs.
+int calib_l2read(const void *buf, size_t bytes, int reps, uint32_t *sink, int blocks, void *stream) {
+    if (buf == nullptr || sink == nullptr || blocks < 1 || reps < 1 || bytes % (16 * 1024) != 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_l2read, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(buf), bytes / 16, reps, sink);
     return hipGetLastError();
 }
 
