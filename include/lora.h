@@ -192,6 +192,15 @@ int lora_unregister(lora_pool p, int slot);
 int lora_set_policy(lora_pool p, lora_mode mode, int threshold);
 int lora_get_policy(lora_pool p, lora_mode *mode, int *threshold);
 
+/* For tests of the in-launch shrink.  Calls of 65 .. 2047 tokens whose GEMM
+ * tiles leave CUs idle compute h on those CUs inside the GEMM launch; the h
+ * consumers of that launch poll a count of finished h units at most `polls`
+ * times and, if it is still short, compute every unit themselves (the same
+ * code, so the same bits).  polls = 0: they never wait and always compute h
+ * themselves; polls = -1: the library's bound (about 0.1-0.3 s).  The
+ * outputs do not depend on it.  LORA_EINVAL for a null pool or polls < -1. */
+int lora_set_shrink_wait_polls(lora_pool p, int polls);
+
 /* ------------------------------------------------------------ hot path -- */
 
 /* y = x W_base^T + per-token LoRA term, asynchronously on `stream`

@@ -96,6 +96,7 @@ struct lora_pool_s {
     std::vector<std::pair<hipStream_t, hipEvent_t>> inflight;
     int policy = LORA_MODE_AUTO;
     int theta = kDefaultTheta;
+    int shrink_wait_polls = -1;  // lora_set_shrink_wait_polls (-1: the kernel's bound)
 
     // Slot-entry publication (register, loader commit): `gate` is recorded on
     // `internal` after the last entry write; until it has completed, every
@@ -355,7 +356,8 @@ size_t carve_call(lora_pool p, int n_tokens, char *base, CallSpace *cs) {
         // The split counters sit in the scratch's own zeroed block (they are
         // back at 0 after every call).
         unsigned *cnt = lora::scratch_split_counters(p->device);
-        cs->split = lora::SplitSpace{cs->part, cnt, lora::MAX_SPLIT_TILES, cnt + lora::MAX_SPLIT_TILES};
+        cs->split = lora::SplitSpace{cs->part, cnt, lora::MAX_SPLIT_TILES, cnt + lora::MAX_SPLIT_TILES,
+                                     p->shrink_wait_polls};
     }
     return off;
 }
@@ -484,7 +486,8 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
 // The pool's own workspace.
 CallSpace pool_space(lora_pool p) {
     return CallSpace{p->ro, p->h, p->part,
-                     lora::SplitSpace{p->part, p->split_cnt, p->split_tiles, p->split_cnt + p->split_tiles}};
+                     lora::SplitSpace{p->part, p->split_cnt, p->split_tiles, p->split_cnt + p->split_tiles,
+                                      p->shrink_wait_polls}};
 }
 
 // Host-side checks shared by lora_apply and lora_apply_noalloc.
@@ -732,6 +735,13 @@ int lora_unregister(lora_pool p, int slot) {
         return hip_fail(e);
     }
     p->book.finish_unregister(slot);
+    return LORA_OK;
+}
+
+int lora_set_shrink_wait_polls(lora_pool p, int polls) {
+    if (p == nullptr || polls < -1) return LORA_EINVAL;
+    std::lock_guard<std::mutex> lk(p->mu);
+    p->shrink_wait_polls = polls;
     return LORA_OK;
 }
 

@@ -294,14 +294,18 @@ __global__ __launch_bounds__(512) void k_gemm_lds(ApplyArgs a, SplitArgs sp) {
         const int P = uniform(a.h_parts);
         const int need = uniform(*a.rv.n_tiles) * P;
         if (threadIdx.x == 0) {
+            // (wait_polls 0: never wait, compute h here.)
             int spins = 0;
-            while (__hip_atomic_load(sp.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                       static_cast<unsigned>(need) &&
-                   spins < FS_SPIN_MAX) {
+            bool short_count = sp.wait_polls == 0 ||
+                               __hip_atomic_load(sp.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                                   static_cast<unsigned>(need);
+            while (short_count && spins < sp.wait_polls) {
                 __builtin_amdgcn_s_sleep(2);
                 ++spins;
+                short_count = __hip_atomic_load(sp.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                              static_cast<unsigned>(need);
             }
-            h_late = spins >= FS_SPIN_MAX;
+            h_late = short_count;
         }
         __syncthreads();
         if (uniform(h_late)) {
@@ -669,6 +673,7 @@ hipError_t launch_dt(const ApplyArgs &a, const SplitSpace &ws, hipStream_t st, L
         sp.cnt = ws.cnt;
         sp.shrink_wgs = tp.shrink_wgs;
         sp.sync = ws.sync;
+        sp.wait_polls = ws.wait_polls < 0 ? FS_SPIN_MAX : ws.wait_polls;
         // The workspace was sized with tiled_part_bytes / tiled_split_tiles.
         const int nc = tp.splits + tp.lora_wg;
         if (nc > 1 && (ws.part == nullptr || ws.cnt == nullptr || sp.tiles > ws.max_tiles))

@@ -204,6 +204,7 @@ struct SplitSpace {
     unsigned *cnt = nullptr;
     int max_tiles = 0;   // counters available at cnt
     unsigned *sync = nullptr;  // [2] the fused shrink's counters (0 between calls)
+    int wait_polls = -1;       // the fused shrink's consumer poll bound (-1: the default)
 };
 struct SplitArgs {
     int splits;
@@ -214,6 +215,7 @@ struct SplitArgs {
     unsigned *cnt;
     int shrink_wgs;      // fused shrink: shrink workgroups after the tiles' contributors
     unsigned *sync;      // fused shrink: [units counted, workgroups done]
+    int wait_polls;      // fused shrink: polls of the count before a consumer computes h itself
 };
 hipError_t launch_gemm_tiled(const ApplyArgs &a, const SplitSpace &ws, hipStream_t st, LaunchEvents ev = {});
 // The static per-device workspace of lora_apply_noalloc (scratch.hip):

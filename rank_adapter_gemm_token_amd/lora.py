@@ -43,7 +43,8 @@ TORCH_DTYPE = {v: k for k, v in DTYPE_OF.items()}
 
 # Every symbol include/lora.h declares, in declaration order.
 EXPORTS = ["lora_pool_create", "lora_pool_destroy", "lora_set_tenant_quota", "lora_register",
-           "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_apply", "lora_apply_noalloc", "lora_route",
+           "lora_unregister", "lora_set_policy", "lora_get_policy", "lora_set_shrink_wait_polls", "lora_apply",
+           "lora_apply_noalloc", "lora_route",
            "lora_last_routing",
            "lora_plan_create", "lora_plan_destroy", "lora_plan_route", "lora_apply_routed",
            "lora_loader_create", "lora_loader_destroy", "lora_load_async", "lora_load_poll", "lora_load_wait",
@@ -85,6 +86,7 @@ _lib.lora_set_tenant_quota.argtypes = [_vp, ctypes.c_int32, ctypes.c_uint64]
 _lib.lora_register.argtypes = [_vp, _i, ctypes.c_int32, _vp, _vp, _i, ctypes.c_float, _vp]
 _lib.lora_unregister.argtypes = [_vp, _i]
 _lib.lora_set_policy.argtypes = [_vp, _i, _i]
+_lib.lora_set_shrink_wait_polls.argtypes = [_vp, _i]
 _lib.lora_get_policy.argtypes = [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i)]
 _lib.lora_apply.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
 _lib.lora_apply_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
@@ -209,6 +211,10 @@ def lora_unregister(pool, slot):
 
 def lora_set_policy(pool, mode, threshold):
     _check(_lib.lora_set_policy(pool, int(mode), int(threshold)), "lora_set_policy")
+
+
+def lora_set_shrink_wait_polls(pool, polls):
+    _check(_lib.lora_set_shrink_wait_polls(pool, int(polls)), "lora_set_shrink_wait_polls")
 
 
 def lora_get_policy(pool):

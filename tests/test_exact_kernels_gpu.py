@@ -299,3 +299,27 @@ def test_split_calls_of_every_plan_on_one_pool():
             assert_close(y.view(torch.bfloat16), ref, inv, "bf16")
     finally:
         p.close()
+
+
+@pytest.mark.parametrize("shape", ["split4", "split_tail1", "split_tail2"])
+def test_in_launch_shrink_fallback_same_bits(shape):
+    # Shapes whose GEMM runs the shrink on idle CUs in the same launch.  With
+    # the poll bound at 0 every h consumer computes all of h itself instead of
+    # waiting for the shrink workgroups: the output must be the same bits, and
+    # the calls after it (default bound) must still agree (the counters end
+    # each call at 0 whichever way h was obtained).
+    x, W, ads, idx = _normal_case(shape, "bf16", 12)
+    p = _pool(shape, "bf16", lora.LORA_MODE_AUTO, ads, theta=0)
+    try:
+        xd, Wd, idd = dev(x), dev(W), dev(idx)
+        base = p.apply(xd, Wd, idd).cpu().view(torch.int16)
+        lora.lora_set_shrink_wait_polls(p.h, 0)
+        for _ in range(2):
+            assert torch.equal(p.apply(xd, Wd, idd).cpu().view(torch.int16), base)
+        lora.lora_set_shrink_wait_polls(p.h, -1)
+        for _ in range(2):
+            assert torch.equal(p.apply(xd, Wd, idd).cpu().view(torch.int16), base)
+        ref, inv = reference(p, x, W, idx)
+        assert_close(base.view(torch.bfloat16), ref, inv, "bf16")
+    finally:
+        p.close()

@@ -82,6 +82,7 @@ def test_validation_before_device_use():
     assert lib.lora_unregister(None, 0) == L.LORA_EINVAL
     assert lib.lora_set_tenant_quota(None, 0, 10) == L.LORA_EINVAL
     assert lib.lora_set_policy(None, 0, 16) == L.LORA_EINVAL
+    assert lib.lora_set_shrink_wait_polls(None, 0) == L.LORA_EINVAL
     assert lib.lora_route(None, None, 0, None, None, None, None, None, None) == L.LORA_EINVAL
     s = L.lora_stats()
     assert lib.lora_pool_stats(None, ctypes.byref(s)) == L.LORA_EINVAL
