@@ -18,6 +18,9 @@ depends on (T, d_in, d_out, dtype) only):
               for the shrink before its tail expand
   split_tail2 96 tiles x 2 splits + 64 shrink workgroups, no LoRA
               workgroup: the last split of a tile waits before the expand
+  split_r64   4 tiles x (6 splits + LoRA workgroup) + 228 shrink
+              workgroups, ranks up to 64 (shrink units of 3-4 rank blocks)
+              and two k parts of h
   split_lora_nofuse  56 tiles x (3 splits + LoRA workgroup) = 224
               workgroups: too few idle CUs, the shrink in a launch of its own
   split_nofuse  384 tiles x 1 split (more than one round of the CUs): the
@@ -63,6 +66,7 @@ SHAPES = {
     "split_xcd": (70, 1024, 192, 6, 16),     # 3 tiles x 4 splits: splits on different XCDs
     "split_tail1": (300, 1024, 4096, 9, 16),     # 128 tiles x 1 split + 128 shrink workgroups
     "split_tail2": (700, 2048, 2048, 9, 16),     # 96 tiles x 2 splits + 64 shrink workgroups
+    "split_r64": (130, 4096, 256, 9, 64),        # in-launch shrink at ranks up to 64, 2 k parts
     "split_lora_nofuse": (1600, 2048, 512, 9, 16),  # 56 tiles x (3 + 1), separate shrink
     "split_nofuse": (1300, 256, 4096, 6, 16),    # 384 tiles: separate (grouped) shrink
     "big": (2048, 256, 256, 12, 64),
@@ -301,7 +305,7 @@ def test_split_calls_of_every_plan_on_one_pool():
         p.close()
 
 
-@pytest.mark.parametrize("shape", ["split4", "split_tail1", "split_tail2"])
+@pytest.mark.parametrize("shape", ["split4", "split_tail1", "split_tail2", "split_r64"])
 def test_in_launch_shrink_fallback_same_bits(shape):
     # Shapes whose GEMM runs the shrink on idle CUs in the same launch.  With
     # the poll bound at 0 every h consumer computes all of h itself instead of
