@@ -168,7 +168,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(ApplyArgs a) {
 // call, loads the other splits' partial sums (agent-coherent loads), adds
 // all of them in split order z = 0, 1, .. (so the sum does not depend on
 // which split finished last), adds the fused expand and stores y.  No
-// workgroup waits for another.  The splits of a tile are numbered so that the
+// workgroup waits for another, except (FS, below) an h consumer's bounded
+// wait for the in-launch shrink.  The splits of a tile are numbered so that the
 // hardware's round-robin dealing of workgroups to the 8 XCDs puts them on one
 // XCD when 8 divides the grid.
 using lds_ptr = __attribute__((address_space(3))) void *;
