@@ -442,7 +442,10 @@ typedef struct {
                            their two launches and record no stage marks
                            between them: route_ms, shrink_ms and expand_ms are
                            0 and gemm_ms is the whole call (with the residual
-                           expand when a bucket runs SEPARATE) */
+                           expand when a bucket runs SEPARATE).  Longer fp16/
+                           bf16 calls may route inside the shrink launch
+                           (route_ms 0, shrink_ms both) or shrink inside the
+                           GEMM launch (shrink_ms 0, gemm_ms both) */
     double expand_ms;   /* separate residual expand */
     double kernel_ms;   /* device time of the base-GEMM kernel itself (fp16/
                            bf16 pools; 0 for fp32) */

@@ -435,33 +435,41 @@ int apply_locked(lora_pool p, const void *x, const void *W_base, const int32_t *
         }
     } else {
         if (ps) ps->staged = true;
-        if (!pre) {
-            HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy, p->theta,
-                                       cs.ro, st));
-            if (!noalloc) {
-                p->last_route_T = n_tokens;
-                p->last_route_stream = st;
-            }
-        }
-        HIP_TRY(mark(1));
         // Split calls whose GEMM grid is one round run the shrink inside the
         // GEMM launch (its k parts are the plan's).
         const int fused_parts = half ? lora::tiled_plan(n_tokens, p->d_in, p->d_out).fuse_parts : 0;
         if (fused_parts > 0) {
             a.shrink_parts = fused_parts;
             a.h_parts = fused_parts;
-        } else {
-            if (half) {
-                // k parts of the shrink; the grouped shrink adds them into part 0
-                // itself (on the counters the split tiles also use, in stream
-                // order, each kernel leaving them at 0), so its consumers read one.
-                const int parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound, n_tokens);
-                a.shrink_g = lora::shrink_group(n_tokens, a.tiles_bound, cs.split.max_tiles);
-                a.shrink_parts = parts;
-                a.h_parts = a.shrink_g > 1 ? 1 : parts;
-            }
-            HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
+        } else if (half) {
+            // k parts of the shrink; the grouped shrink adds them into part 0
+            // itself (on the counters the split tiles also use, in stream
+            // order, each kernel leaving them at 0), so its consumers read one.
+            const int parts = lora::tiled_h_parts(p->d_in, p->Rp, a.tiles_bound, n_tokens);
+            a.shrink_g = lora::shrink_group(n_tokens, a.tiles_bound, cs.split.max_tiles);
+            a.shrink_parts = parts;
+            a.h_parts = a.shrink_g > 1 ? 1 : parts;
         }
+        // A call routed here whose shrink has a launch of its own, one tile a
+        // workgroup, routes inside that launch when the call and the grid are
+        // small enough (one launch fewer).
+        const bool route_in_shrink =
+            !pre && half && fused_parts == 0 && a.shrink_g == 1 && n_tokens <= lora::ROUTE_SHRINK_MAX_T &&
+            static_cast<long>(a.tiles_bound) * a.shrink_parts <= lora::ROUTE_SHRINK_MAX_WGS;
+        if (!pre) {
+            if (!route_in_shrink)
+                HIP_TRY(lora::launch_route(token_adapter_idx, n_tokens, p->S, p->slots_dev, p->R, p->policy,
+                                           p->theta, cs.ro, st));
+            if (!noalloc) {
+                p->last_route_T = n_tokens;
+                p->last_route_stream = st;
+            }
+        }
+        HIP_TRY(mark(1));
+        if (route_in_shrink)
+            HIP_TRY(lora::launch_route_shrink16(a, token_adapter_idx, p->R, p->theta, cs.ro, st));
+        else if (fused_parts == 0)
+            HIP_TRY(half ? lora::launch_shrink16(a, st) : lora::launch_shrink(a, st));
         HIP_TRY(mark(2));
         if (half) {
             if (!any_separate && kev.stop == nullptr) {

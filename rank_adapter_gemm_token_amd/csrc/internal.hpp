@@ -116,6 +116,16 @@ struct ApplyArgs {
 
 hipError_t launch_shrink(const ApplyArgs &a, hipStream_t st);
 hipError_t launch_shrink16(const ApplyArgs &a, hipStream_t st);
+// The routing and the fp16/bf16 shrink (one bucket tile a workgroup) in one
+// launch: every workgroup routes the call into its own LDS, workgroup 0
+// writes `out` as launch_route does (R, theta as there).  For calls of at
+// most ROUTE_SHRINK_MAX_T tokens whose shrink grid (a.tiles_bound x
+// a.shrink_parts) is at most ROUTE_SHRINK_MAX_WGS workgroups: each of them
+// repeats the routing, so a larger grid would repeat it over more rounds.
+constexpr int ROUTE_SHRINK_MAX_T = 1024;
+constexpr int ROUTE_SHRINK_MAX_WGS = 512;
+hipError_t launch_route_shrink16(const ApplyArgs &a, const int32_t *idx, int R, int theta, const RouteOut &out,
+                                 hipStream_t st);
 // k parts of the fp16/bf16 shrink on the tiled path (h_parts) for a call of
 // at most `tiles` bucket tiles; consumers add the parts in order.
 constexpr int MAX_HPARTS = 8;

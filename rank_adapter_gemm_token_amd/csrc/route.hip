@@ -26,17 +26,27 @@
 // histogram over all of them:
 //   offset[key] + (tokens of key in earlier chunks) + (in earlier waves) + rank.
 // Either way ties keep ascending token order, which makes the result unique.
+//
+// Calls of at most 1024 tokens that route in the call and shrink in a launch
+// of their own (fp16/bf16) route inside the shrink launch instead
+// (k_route_shrink): every shrink workgroup of 256 threads derives the whole
+// routing into its own LDS with the same one-pass code at 4 waves, reads its
+// bucket tile from it and runs the shrink unit; workgroup 0 also writes the
+// routing arrays for the later kernels.  No workgroup waits for another, and
+// the arrays are the ones k_route writes (the order is unique).
+#include "epilogue.hpp"
 #include "internal.hpp"
 
 namespace lora {
 
 namespace {
 
-constexpr int RT = 1024;
-constexpr int RW = RT / 64;
+constexpr int RT = 1024;          // threads of k_route
 constexpr int KEY_CAP = 32768;   // tokens whose keys stay in LDS (2 bytes each)
 constexpr int IDX_UNROLL = 4;    // index loads per thread in flight
-constexpr int ONE_PASS_T = RT * IDX_UNROLL;  // calls routed in one pass
+constexpr int RS_T = 256;        // threads of k_route_shrink
+constexpr int RS_MAX_T = RS_T * IDX_UNROLL;  // its calls (one pass)
+static_assert(RS_MAX_T == ROUTE_SHRINK_MAX_T, "k_route_shrink routes its calls in one pass");
 
 // Global-memory views of the output pointers.  Stores through a generic
 // pointer may alias LDS in the compiler's eyes, so every later LDS read would
@@ -80,21 +90,45 @@ __device__ __forceinline__ int key_of(int32_t v, int S, const SlotDev *__restric
     return S + 1;
 }
 
-__global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, int T, int S,
-                                               const SlotDev *__restrict__ slots, int R,
-                                               int policy, int theta, RouteOut out) {
-    __shared__ int s_cnt[MAX_KEYS];
-    __shared__ int s_off[MAX_KEYS];
-    __shared__ int s_run[MAX_KEYS];
-    __shared__ int s_seg[MAX_KEYS];
-    __shared__ int s_tile[MAX_KEYS];
-    __shared__ unsigned short s_wc[RW][MAX_KEYS];
-    __shared__ int s_tot[4];  // buckets, tiles, fused buckets, separate buckets
-    __shared__ int s_rows[2]; // padded rows, true rows
-    __shared__ unsigned char s_act[MAX_KEYS];     // slot k is ACTIVE
-    __shared__ unsigned short s_rank[MAX_KEYS];   // slot k's true rank
-    __shared__ unsigned short s_key[KEY_CAP];     // token -> key (T <= KEY_CAP)
+// Routing state in LDS for NT threads; the per-token key store only when
+// calls longer than one pass are routed (MULTI).
+template <int NT, bool MULTI>
+struct RouteLds {
+    int cnt[MAX_KEYS];
+    int off[MAX_KEYS];
+    int run[MAX_KEYS];
+    int seg[MAX_KEYS];
+    int tile[MAX_KEYS];
+    unsigned short wc[NT / 64][MAX_KEYS];
+    int tot[4];   // buckets, tiles, fused buckets, separate buckets
+    int rows[2];  // padded rows, true rows
+    unsigned char act[MAX_KEYS];    // slot k is ACTIVE
+    unsigned short rank[MAX_KEYS];  // slot k's true rank
+    unsigned short key[MULTI ? KEY_CAP : 1];  // token -> key (T <= KEY_CAP)
+};
 
+// The routing of one call by one workgroup of NT threads.  publish: write the
+// arrays of `out` (else only L is filled); perm_lds (when not null): the
+// sorted position -> token map also in LDS.  Without MULTI, T <= NT *
+// IDX_UNROLL (one pass).  Ends with a barrier: L (and perm_lds) are complete.
+template <int NT, bool MULTI>
+__device__ __forceinline__ void route_body(const int32_t *__restrict__ idx, int T, int S,
+                                           const SlotDev *__restrict__ slots, int R, int policy, int theta,
+                                           const RouteOut &out, RouteLds<NT, MULTI> &L, bool publish,
+                                           int *perm_lds) {
+    constexpr int RW = NT / 64;
+    constexpr int ONE_PASS_T = NT * IDX_UNROLL;  // calls routed in one pass
+    auto &s_cnt = L.cnt;
+    auto &s_off = L.off;
+    auto &s_run = L.run;
+    auto &s_seg = L.seg;
+    auto &s_tile = L.tile;
+    auto &s_wc = L.wc;
+    auto &s_tot = L.tot;
+    auto &s_rows = L.rows;
+    auto &s_act = L.act;
+    auto &s_rank = L.rank;
+    auto &s_key = L.key;
     const int K = S + 2;
     const gptr<int32_t> o_counts = global(out.counts), o_offsets = global(out.offsets), o_perm = global(out.perm),
                         o_segs = global(out.segs), o_pos_seg = global(out.pos_seg), o_tok_pos = global(out.tok_pos),
@@ -103,11 +137,11 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    const bool one_pass = T <= ONE_PASS_T;
+    const bool one_pass = !MULTI || T <= ONE_PASS_T;
     // Tokens per wave in one pass (a multiple of 64), and this lane's tokens:
     // wave w's range, 64 at a time (one pass), or chunk-strided (chunks).
-    const int nsub = (T + RT - 1) / RT;  // 0 .. IDX_UNROLL in one pass
-    auto tok = [&](int u) { return one_pass ? wave * 64 * nsub + u * 64 + lane : u * RT + tid; };
+    const int nsub = (T + NT - 1) / NT;  // 0 .. IDX_UNROLL in one pass
+    auto tok = [&](int u) { return one_pass ? wave * 64 * nsub + u * 64 + lane : u * NT + tid; };
 
     // The first round of token indices and every slot's state and rank are
     // requested together, before the LDS set-up, in one round trip.  (T = 0:
@@ -116,18 +150,18 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     if (T > 0) {
 #pragma unroll
         for (int u = 0; u < IDX_UNROLL; ++u) vi[u] = idx[min(tok(u), T - 1)];
-        if (out.idx_copy != nullptr) {
+        if (publish && out.idx_copy != nullptr) {
 #pragma unroll
             for (int u = 0; u < IDX_UNROLL; ++u)
                 if ((!one_pass || u < nsub) && tok(u) < T) out.idx_copy[tok(u)] = vi[u];
         }
     }
-    for (int k = tid; k < S; k += RT) {
+    for (int k = tid; k < S; k += NT) {
         const SlotDev sd = slots[k];
         s_act[k] = sd.state == SLOT_ACTIVE;
         s_rank[k] = static_cast<unsigned short>(sd.rank);
     }
-    for (int k = tid; k < K; k += RT) {
+    for (int k = tid; k < K; k += NT) {
         s_cnt[k] = 0;
         s_run[k] = 0;
         for (int w = 0; w < RW; ++w) s_wc[w][k] = 0;
@@ -166,7 +200,7 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
         __syncthreads();
         // Per key: the waves' counts become each wave's start within the key
         // (exclusive prefix in wave order), their sum the key's count.
-        for (int k = tid; k < K; k += RT) {
+        for (int k = tid; k < K; k += NT) {
             int c[RW];
 #pragma unroll
             for (int w = 0; w < RW; ++w) c[w] = s_wc[w][k];
@@ -178,7 +212,7 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
             }
             s_cnt[k] = run;
         }
-    } else {
+    } else if constexpr (MULTI) {
         // Keys.  Every index is read once (IDX_UNROLL per thread in flight); a
         // token's key is an LDS lookup of its slot's state, kept in LDS for the
         // scatter when T <= KEY_CAP.  The histogram adds one count per distinct
@@ -186,20 +220,20 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
         // key bit and the lowest of them adds their number (one LDS atomic per
         // key, instead of one per token: a wave of one adapter's tokens would
         // otherwise serialise 64 atomics on one address).
-        for (int t0 = 0; t0 < T; t0 += RT * IDX_UNROLL) {
+        for (int t0 = 0; t0 < T; t0 += NT * IDX_UNROLL) {
             if (t0 > 0) {
 #pragma unroll
-                for (int u = 0; u < IDX_UNROLL; ++u) vi[u] = idx[min(t0 + u * RT + tid, T - 1)];
+                for (int u = 0; u < IDX_UNROLL; ++u) vi[u] = idx[min(t0 + u * NT + tid, T - 1)];
                 if (out.idx_copy != nullptr) {
 #pragma unroll
                     for (int u = 0; u < IDX_UNROLL; ++u)
-                        if (t0 + u * RT + tid < T) out.idx_copy[t0 + u * RT + tid] = vi[u];
+                        if (t0 + u * NT + tid < T) out.idx_copy[t0 + u * NT + tid] = vi[u];
                 }
             }
 #pragma unroll
             for (int u = 0; u < IDX_UNROLL; ++u) {
-                if (t0 + u * RT >= T) break;  // (uniform) no token in this round
-                const int t = t0 + u * RT + tid;
+                if (t0 + u * NT >= T) break;  // (uniform) no token in this round
+                const int t = t0 + u * NT + tid;
                 const bool v = t < T;
                 const int key = !v ? K
                                    : ((vi[u] == -1) ? S : ((vi[u] >= 0 && vi[u] < S && s_act[vi[u]]) ? vi[u] : S + 1));
@@ -262,7 +296,7 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     __syncthreads();
 
     // Per-key outputs: counts, offsets, bucket records.
-    for (int k = tid; k < K; k += RT) {
+    for (int k = tid; publish && k < K; k += NT) {
         const int n = s_cnt[k];
         o_counts[k] = n;
         o_offsets[k] = s_off[k];
@@ -283,8 +317,8 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     // mostly others): tile j belongs to the last key k < S whose first tile
     // index s_tile[k] is at most j (keys without tiles share their
     // successor's index and are passed over).
-    if (out.tiles != nullptr) {
-        for (int j = RT - 1 - tid; j < s_tot[1]; j += RT) {
+    if (publish && out.tiles != nullptr) {
+        for (int j = NT - 1 - tid; j < s_tot[1]; j += NT) {
             int lo = 0, hi = S;  // the first key whose first tile is past j
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
@@ -308,16 +342,19 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
             const int key = okey[u];
             const int pos = s_off[key] + s_wc[wave][key] + orank[u];
             if (pos >= 0 && pos < T) {  // always true; keeps a logic error in bounds
-                o_perm[pos] = t;
-                if (out.pos_seg != nullptr) o_pos_seg[pos] = s_seg[key];
-                if (out.tok_pos != nullptr) o_tok_pos[t] = pos;
-                if (out.tok_seg != nullptr) o_tok_seg[t] = s_seg[key];
+                if (perm_lds != nullptr) perm_lds[pos] = t;
+                if (publish) {
+                    o_perm[pos] = t;
+                    if (out.pos_seg != nullptr) o_pos_seg[pos] = s_seg[key];
+                    if (out.tok_pos != nullptr) o_tok_pos[t] = pos;
+                    if (out.tok_seg != nullptr) o_tok_seg[t] = s_seg[key];
+                }
             }
         }
     }
 
-    // Stable scatter, one chunk of RT tokens at a time.
-    for (int c0 = 0; !one_pass && c0 < T; c0 += RT) {
+    // Stable scatter, one chunk of NT tokens at a time (k_route only).
+    for (int c0 = 0; MULTI && !one_pass && c0 < T; c0 += NT) {
         const int t = c0 + tid;
         const bool v = t < T;
         const int key = !v ? K : (keep ? static_cast<int>(s_key[t]) : key_of(idx[t], S, slots));
@@ -337,7 +374,7 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
             }
         }
         __syncthreads();
-        for (int k = tid; k < K; k += RT) {
+        for (int k = tid; k < K; k += NT) {
             int add = 0;
             for (int w = 0; w < RW; ++w) {
                 add += s_wc[w][k];
@@ -349,7 +386,7 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     }
 
     __syncthreads();
-    if (tid == 0) {
+    if (publish && tid == 0) {
         *global(out.n_seg) = s_tot[0];
         if (out.n_tiles != nullptr) *global(out.n_tiles) = s_tot[1];
         if (out.stats != nullptr) {
@@ -369,6 +406,58 @@ __global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, i
     }
 }
 
+__global__ __launch_bounds__(RT) void k_route(const int32_t *__restrict__ idx, int T, int S,
+                                               const SlotDev *__restrict__ slots, int R,
+                                               int policy, int theta, RouteOut out) {
+    __shared__ RouteLds<RT, true> L;
+    route_body<RT, true>(idx, T, S, slots, R, policy, theta, out, L, true, nullptr);
+}
+
+// Routing and shrink in one launch, for calls of at most RS_MAX_T tokens:
+// unit (tile, k part) per workgroup as k_shrink, each workgroup routing the
+// whole call first (route_body into its own LDS, workgroup 0 publishing the
+// arrays), then finding its tile there as the routing's tile list does.
+template <int DT, int RB>
+__global__ __launch_bounds__(RS_T) void k_route_shrink(const int32_t *__restrict__ idx, int R, int theta,
+                                                       RouteOut out, ApplyArgs a) {
+    __shared__ RouteLds<RS_T, false> L;
+    __shared__ int s_perm[RS_MAX_T];
+    __shared__ u32x4_t lds[4 * RB * 64];
+    const int S = a.S;
+    route_body<RS_T, false>(idx, a.T, S, a.slots, R, a.policy, theta, out, L, blockIdx.x == 0, s_perm);
+    const int tile = blockIdx.x / a.shrink_parts;
+    const int part = blockIdx.x % a.shrink_parts;
+    if (tile >= L.tot[1]) return;
+    // The last key k < S whose first tile index is at most `tile`.
+    int lo = 0, hi = S;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (L.tile[mid] <= tile) lo = mid + 1;
+        else hi = mid;
+    }
+    const int key = lo - 1;
+    const int row0 = L.off[key] + (tile - L.tile[key]) * TILE_ROWS;
+    const int rows = min(TILE_ROWS, L.off[key] + L.cnt[key] - row0);
+    // Rank blocks that hold the slot's true rank.
+    const int nrb = uniform(min(RB, (static_cast<int>(L.rank[key]) + 15) / 16));
+    if (RB >= 4 && nrb == 4) shrink_unit<DT, (RB >= 4 ? 4 : 1), 4>(a, key, row0, rows, s_perm, part, lds);
+    else if (RB >= 3 && nrb == 3) shrink_unit<DT, (RB >= 3 ? 3 : 1), 4>(a, key, row0, rows, s_perm, part, lds);
+    else if (RB >= 2 && nrb == 2) shrink_unit<DT, (RB >= 2 ? 2 : 1), 4>(a, key, row0, rows, s_perm, part, lds);
+    else shrink_unit<DT, 1, 4>(a, key, row0, rows, s_perm, part, lds);
+}
+
+template <int DT>
+hipError_t route_shrink_rb(const ApplyArgs &a, dim3 grid, const int32_t *idx, int R, int theta, const RouteOut &out,
+                           hipStream_t st) {
+    switch ((a.R + 15) / 16) {
+        case 1: hipLaunchKernelGGL((k_route_shrink<DT, 1>), grid, dim3(RS_T), 0, st, idx, R, theta, out, a); break;
+        case 2: hipLaunchKernelGGL((k_route_shrink<DT, 2>), grid, dim3(RS_T), 0, st, idx, R, theta, out, a); break;
+        case 3: hipLaunchKernelGGL((k_route_shrink<DT, 3>), grid, dim3(RS_T), 0, st, idx, R, theta, out, a); break;
+        default: hipLaunchKernelGGL((k_route_shrink<DT, 4>), grid, dim3(RS_T), 0, st, idx, R, theta, out, a); break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_route(const int32_t *idx, int T, int S, const SlotDev *slots, int R, int policy,
@@ -376,6 +465,17 @@ hipError_t launch_route(const int32_t *idx, int T, int S, const SlotDev *slots, 
     LORA_LAUNCH((LaunchEvents{nullptr, done}), k_route, dim3(1), dim3(RT), 0, st, idx, T, S, slots, R, policy, theta,
                 out);
     return hipGetLastError();
+}
+
+hipError_t launch_route_shrink16(const ApplyArgs &a, const int32_t *idx, int R, int theta, const RouteOut &out,
+                                 hipStream_t st) {
+    const long wgs = static_cast<long>(a.tiles_bound) * a.shrink_parts;
+    if (a.T < 1 || a.T > RS_MAX_T || a.S < 1 || a.S > MAX_KEYS - 2 || a.shrink_g != 1 || a.shrink_parts < 1 ||
+        a.h_by_token != 0 || a.d_in % 32 != 0 || a.tiles_bound != max_tiles(a.T, a.S) || wgs > ROUTE_SHRINK_MAX_WGS)
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(wgs));
+    return a.dtype == DT_F16 ? route_shrink_rb<DT_F16>(a, grid, idx, R, theta, out, st)
+                             : route_shrink_rb<DT_BF16>(a, grid, idx, R, theta, out, st);
 }
 
 }  // namespace lora

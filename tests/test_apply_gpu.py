@@ -176,8 +176,10 @@ def _max_case(dtype, T, d_in, d_out, S, R, used, seed):
 
 # The largest pool (LORA_MAX_SLOTS slots, LORA_MAX_RANK rank) on every path:
 # decode (d_out = 128: two column groups take slots 0..1023 in turn), the split
-# 256-row tiles and the unsplit ones (a call of 4100 tokens, rows sampled).
+# 256-row tiles (at 256 x 4096 -> 4096 routed inside the shrink launch, rows
+# sampled) and the unsplit ones (a call of 4100 tokens, rows sampled).
 @pytest.mark.parametrize("dtype,T,d_in,d_out", [("f16", 64, 256, 128), ("bf16", 700, 256, 256),
+                                                ("f16", 256, 4096, 4096),
                                                 ("bf16", 4100, 256, 256), ("f32", 33, 64, 64)])
 def test_max_slots_and_rank(dtype, T, d_in, d_out):
     S, R = lora.LORA_MAX_SLOTS, lora.LORA_MAX_RANK
@@ -187,7 +189,8 @@ def test_max_slots_and_rank(dtype, T, d_in, d_out):
         p.register_all(ads)
         y = p.apply(dev(x), dev(W), dev(idx))
         torch.cuda.synchronize()
-        rows = None if T <= 1024 else sample_rows(T, 64, seed=1, must=[0, T - 1])
+        big = T > 1024 or d_in * d_out > 1 << 20
+        rows = None if not big else sample_rows(T, 64, seed=1, must=[0, T - 1])
         y_ref, inv = reference(p, x, W, idx, rows=rows)
         got = y.cpu() if rows is None else y.cpu()[torch.as_tensor(rows)]
         assert_close(got, y_ref, inv, dtype)

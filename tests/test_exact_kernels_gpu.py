@@ -69,6 +69,8 @@ SHAPES = {
     "split_r64": (130, 4096, 256, 9, 64),        # in-launch shrink at ranks up to 64, 2 k parts
     "split_lora_nofuse": (1600, 2048, 512, 9, 16),  # 56 tiles x (3 + 1), separate shrink
     "split_nofuse": (1300, 256, 4096, 6, 16),    # 384 tiles: separate (grouped) shrink
+    "split_route_shrink": (300, 4096, 2048, 9, 16),  # 64 tiles x (3 + 1), routing in the shrink launch
+    "tiled_route_shrink": (513, 192, 128, 40, 24),   # unsplit tiles, routing in the shrink launch
     "big": (2048, 256, 256, 12, 64),
     "tiled": (70, 128, 192, 6, 16),
 }
@@ -236,7 +238,8 @@ def test_integer_inputs_exact(shape, dtype, limit, policy):
 # Decode calls keep partial sums and h in the pool's workspace between the
 # GEMM and its epilogue launch; split calls with the shrink in the GEMM
 # launch count its units on counters that every call leaves at 0.
-DECODE_SHAPES = ["decode64", "decode5", "decodeS70", "split4", "split_tail1", "split_tail2"]
+DECODE_SHAPES = ["decode64", "decode5", "decodeS70", "split4", "split_tail1", "split_tail2",
+                 "split_route_shrink", "tiled_route_shrink"]
 
 
 @pytest.mark.parametrize("shape", DECODE_SHAPES)

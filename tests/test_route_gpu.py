@@ -91,16 +91,17 @@ def test_route_edge_cases(T, dtype):
         p.close()
 
 
-# What lora_apply itself routed with: the decode epilogue (fp16/bf16, T <= 64)
-# and the routing kernel (more tokens), under every policy.
+# What lora_apply itself routed with: the decode epilogue (fp16/bf16, T <= 64),
+# the routing inside the shrink launch (65 .. 1024 tokens on these pools) and
+# the routing kernel (more tokens), under every policy.
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("T", [1, 2, 33, 63, 64, 65, 300])
+@pytest.mark.parametrize("T", [1, 2, 33, 63, 64, 65, 300, 769, 1024, 1025])
 @pytest.mark.parametrize("policy,theta", [(0, 0), (0, 3), (1, 16), (2, 16)])
 def test_applied_routing_bit_exact(T, dtype, policy, theta):
     S = 12
     active = np.ones(S, np.int32)
     active[[3, 7]] = 0
-    p = _pool_with_slots(S, active, 512, policy, theta, dtype=dtype)
+    p = _pool_with_slots(S, active, 1100, policy, theta, dtype=dtype)
     try:
         rng = np.random.default_rng(T + 1000 * policy + theta)
         for name, idx in _edge(T, S, rng).items():
@@ -123,13 +124,15 @@ def test_applied_routing_workloads():
 
 
 def test_applied_routing_max_slots():
-    # 1024 slots, half registered: keys up to 1025 on the small-call routing.
+    # 1024 slots, half registered: keys up to 1025 on the small-call routing
+    # (T <= 64), the routing inside the shrink launch (65, 200: grids of at
+    # most 512 workgroups) and the routing kernel (600: a larger grid).
     S = 1024
     rng = np.random.default_rng(6)
     active = (rng.random(S) < 0.5).astype(np.int32)
-    p = _pool_with_slots(S, active, 64)
+    p = _pool_with_slots(S, active, 600)
     try:
-        for T in (1, 64):
+        for T in (1, 64, 65, 200, 600):
             _compare_applied(p, rng.integers(-1, S + 2, size=T), active)
             _compare(p, rng.integers(-1, S + 2, size=T), active)
     finally:
