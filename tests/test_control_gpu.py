@@ -250,6 +250,21 @@ def test_stage_profile_counts_calls_and_stages():
         assert lora.lora_profile_read(p.h)["calls"] == 0
     finally:
         p.close()
+    # 300 tokens on 4096 -> 2048 route inside the shrink launch: the route
+    # stage holds no launch, the shrink stage both.
+    p = Pool(4096, 2048, 16, 2, 300, "f16")
+    try:
+        A, B = _adapter(4096, 2048, 16)
+        p.register(1, A, B, 16, 32.0)
+        W = dev(torch.randn(2048, 4096).to(torch.float16) / 64)
+        lora.lora_profile_enable(p.h, 1, 8)
+        for _ in range(2):
+            p.apply(dev(torch.randn(300, 4096).to(torch.float16)), W, dev(torch.ones(300, dtype=torch.int32)))
+        r = lora.lora_profile_read(p.h)
+        assert r["calls"] == 2 and r["gemm_ms"] > 0 and r["shrink_ms"] > r["route_ms"] >= 0
+        assert 0 < r["kernel_ms"] <= r["gemm_ms"] + 1e-3
+    finally:
+        p.close()
 
 
 def test_default_policy_is_the_gfx950_threshold():

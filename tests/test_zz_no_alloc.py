@@ -39,10 +39,12 @@ def _bits(y):
 
 # (dtype, d_in, d_out, S, R, first T, second T): decode, split (WC 4 then 2),
 # the unsplit 256-row tiles then the split path, off-grid tiles then decode,
-# fp32.
+# fp32; the routing inside the shrink launch ahead of split tiles and ahead of
+# off-grid tiles.
 CASES = [("f16", 4096, 1024, 6, 16, 64, 16), ("bf16", 1024, 512, 9, 32, 300, 100),
          ("bf16", 256, 256, 12, 64, 2048, 2000), ("f16", 128, 192, 6, 16, 70, 33),
-         ("f32", 256, 256, 4, 8, 16, 5)]
+         ("f32", 256, 256, 4, 8, 16, 5), ("f16", 4096, 2048, 9, 16, 300, 80),
+         ("bf16", 192, 128, 40, 24, 513, 100)]
 
 
 @pytest.mark.parametrize("dtype,d_in,d_out,S,R,T1,T2", CASES)
