@@ -217,6 +217,20 @@ def test_stats_zero_pad_fraction():
         assert st["last_lora_rows_true"] == 8 + 8 + 32
         assert abs(st["last_zero_pad_fraction"] - (1 - 48 / 192)) < 1e-12
         assert p.poll_errors() == 1
+        # 130 tokens on 64 x 64 route inside the shrink launch (workgroup 0
+        # writes the statistics and the error count): the same figures.
+        p.close()
+        p = Pool(64, 64, 64, 3, 130, "bf16")
+        for s, r in enumerate([8, 32, 64]):
+            A, B = _adapter(64, 64, r, s, torch.bfloat16)
+            p.register(s, A, B, r, 2.0 * r)
+        idx = torch.tensor([0, 0, 1, -1, 7] * 26, dtype=torch.int32)
+        p.apply(dev(torch.randn(130, 64).to(torch.bfloat16)), dev(torch.randn(64, 64).to(torch.bfloat16)), dev(idx))
+        st = p.stats()
+        assert st["last_tokens"] == 130 and st["last_adapters"] == 2
+        assert st["last_lora_rows_padded"] == 3 * 26 * 64
+        assert st["last_lora_rows_true"] == (8 + 8 + 32) * 26
+        assert p.poll_errors() == 26
     finally:
         p.close()
 
