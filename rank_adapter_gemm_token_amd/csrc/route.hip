@@ -28,12 +28,13 @@
 // Either way ties keep ascending token order, which makes the result unique.
 //
 // Calls of at most 1024 tokens that route in the call and shrink in a launch
-// of their own (fp16/bf16) route inside the shrink launch instead
-// (k_route_shrink): every shrink workgroup of 256 threads derives the whole
-// routing into its own LDS with the same one-pass code at 4 waves, reads its
-// bucket tile from it and runs the shrink unit; workgroup 0 also writes the
-// routing arrays for the later kernels.  No workgroup waits for another, and
-// the arrays are the ones k_route writes (the order is unique).
+// of their own (fp16/bf16, one bucket tile a workgroup, at most 512
+// workgroups) route inside the shrink launch instead (k_route_shrink): every
+// shrink workgroup of 256 threads derives the whole routing into its own LDS
+// with the same one-pass code at 4 waves, reads its bucket tile from it and
+// runs the shrink unit; workgroup 0 also writes the routing arrays for the
+// later kernels.  No workgroup waits for another, and the arrays are the
+// ones k_route writes (the order is unique).
 #include "epilogue.hpp"
 #include "internal.hpp"
 
