@@ -20,10 +20,13 @@ from rank_adapter_gemm_token_amd import lora
 
 pytestmark = pytest.mark.gpu
 
-D, T, S, R = 1024, 64, 4, 16
+S, R = 4, 16
+# (D, T): a decode call on 1024 x 1024, and 300 tokens on 192 x 192, which
+# route inside the shrink launch (every workgroup reading the slot table).
+SHAPES = [(1024, 64), (192, 300)]
 
 
-def _setup(seed):
+def _setup(seed, D=1024, T=64):
     rng = np.random.default_rng(seed)
     x = torch.from_numpy(rng.standard_normal((T, D))).to(torch.float16)
     W = torch.from_numpy(rng.standard_normal((D, D)) / np.sqrt(D)).to(torch.float16)
@@ -37,6 +40,7 @@ def _setup(seed):
 def _check_outputs(p, x, W, idx, ys):
     """Each output: slot-2 rows all NaN (not yet registered) or correct; the
     switch from NaN to correct happens once."""
+    T = idx.numel()
     ref, _ = reference(p, x, W, idx)  # slot 2 registered in p.adapters
     two = (idx == 2).numpy()
     other_inv = np.zeros(T, bool)
@@ -57,9 +61,10 @@ def _check_outputs(p, x, W, idx, ys):
     return n_nan
 
 
+@pytest.mark.parametrize("D,T", SHAPES)
 @pytest.mark.parametrize("seed", [0, 1])
-def test_register_during_applies(seed):
-    x, W, ads, idx = _setup(seed)
+def test_register_during_applies(seed, D, T):
+    x, W, ads, idx = _setup(seed, D, T)
     p = Pool(D, D, R, S, T, "f16")
     try:
         for s in (0, 1, 3):
@@ -101,8 +106,9 @@ def test_register_during_applies(seed):
         p.close()
 
 
-def test_loader_commit_during_applies():
-    x, W, ads, idx = _setup(5)
+@pytest.mark.parametrize("D,T", SHAPES)
+def test_loader_commit_during_applies(D, T):
+    x, W, ads, idx = _setup(5, D, T)
     p = Pool(D, D, R, S, T, "f16")
     ld = lora.lora_loader_create(R * 2 * D * 2)
     try:
